@@ -1,0 +1,48 @@
+"""CPU oracle for the FP8 E4M3 amax / scale / cast / scaled-GEMM path.
+
+THIS PACKAGE IS TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call it.  The product
+path (the HIP library and its Python binding) never imports it and shares no
+code, table or helper with it.
+
+It is a plain, slow, obviously correct restatement of what the pages define:
+
+* ``e4m3``  - the OCP "e4m3fn" 8-bit float (1 sign, 4 exponent, 3 mantissa bits,
+  no infinities, largest finite value 448): decoding from the bit fields, and a
+  saturating round-to-nearest-even encoder that searches by value.
+  Sources: "Что такое FP8 инференс на H100 (Transformer Engine)?" §2 (E4M3 for
+  inference) and §3 step 3 (448 is the E4M3 maximum); §5 (range -448..448);
+  "FP8混合精度推理" §2 (4 exponent bits, 3 mantissa bits).
+* ``quant`` - amax (largest magnitude) per tensor, per 1x128 token group and per
+  128x128 weight block; scale = amax / 448 in float32; x / scale rounded to
+  e4m3.  Sources: the Transformer Engine page §3 steps 2-4 and its pseudocode;
+  "FP8 chi tiết" (Transformers fine-grained FP8 page), opening bullets.
+* ``gemm``  - the FP8 x FP8 product accumulated exactly in float64, multiplied by
+  scale_A * scale_B per tensor or per 128-wide K slab, and the north-star
+  tolerance check.  Sources: the Transformer Engine page §3 steps 5-6 and its
+  pseudocode; "FP8 chi tiết", opening bullets.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
+pages print (tests/golden), closed forms, brute force over all 256 codes, exact
+rational arithmetic and library special cases.  No function is "parity
+unpinned".
+
+Readings of points the pages leave open are listed in each function's
+docstring (zero amax -> scale 1, NaN -> 0x7F, saturation at 448, fp32 IEEE
+division, operand layout C = A @ B^T).
+"""
+
+from .e4m3 import (E4M3_MAX, decode_e4m3, positive_values, encode_e4m3,
+                   nonneg_breakpoints)
+from .quant import (input_to_f32, amax_per_tensor, amax_groups, scale_from_amax,
+                    quantize_per_tensor, quantize_groups, quantize_with_scale)
+from .gemm import (gemm_tensorwise_ref, gemm_blockwise_ref, bound_tensorwise,
+                   bound_blockwise, output_ulp, check_gemm)
+
+__all__ = [
+    "E4M3_MAX", "decode_e4m3", "positive_values", "encode_e4m3", "nonneg_breakpoints",
+    "input_to_f32", "amax_per_tensor", "amax_groups", "scale_from_amax",
+    "quantize_per_tensor", "quantize_groups", "quantize_with_scale",
+    "gemm_tensorwise_ref", "gemm_blockwise_ref", "bound_tensorwise", "bound_blockwise",
+    "output_ulp", "check_gemm",
+]
