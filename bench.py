@@ -1,0 +1,253 @@
+"""Throughput of the FP8 E4M3 scaled-GEMM hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: amax + scale + cast of
+the activations (per tensor, or per 1x128 token group), then the FP8 x FP8 GEMM with
+float32 accumulation and the scale epilogue.  Weights are quantized once before timing
+(as a serving stack does at load time), except in the small per-tensor workload, where
+both operands are quantized on every call.
+
+Inputs stay resident in HBM; each step reads a different copy of the input set from a
+rotation whose footprint exceeds 1 GiB, so reads come from HBM rather than the 256 MB
+Infinity Cache.
+
+Prints one JSON line.  `value` is the whole step's throughput (TFLOP/s including the
+activation quantize; GB/s for M <= 16 decode), `roofline` rates the dominant kernel
+(the GEMM) from HIP events around each of its launches in the timed region, and
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-GEMM TFLOP/s incl. quantize (% MFMA FP8 peak); decode GB/s (% HBM)"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, 5.0 PFLOP/s
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, 8 TB/s
+DEFAULT_WORKLOAD = "tinyllama_upproj_prefill"
+ROTATION_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--m", type=int, default=None, help="M variant of the workload (default: largest)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, M):
+    """ABI-level bytes of one step: A read as bf16, qA written and read, scales, W read
+    as FP8 with its scales, C written; plus B's quantize when it runs every call."""
+    N, K = w.n, w.k
+    if w.mode == "tensorwise":
+        sa_bytes, sb_bytes = 4, 4
+    else:
+        sa_bytes, sb_bytes = M * (K // 128) * 4, -(-N // 128) * (K // 128) * 4
+    quant_a = 2 * M * K + M * K + sa_bytes
+    gemm = M * K + sa_bytes + N * K + sb_bytes + 2 * M * N
+    quant_b = (2 * N * K + N * K + sb_bytes) if w.quantize_b_per_call else 0
+    return quant_a + gemm + quant_b, gemm
+
+
+def cpu_baseline(w, a_bits, b_bits, budget_s=20.0):
+    """The oracle's quantize(A) + scaled GEMM on the host, on a row sample of A sized to
+    roughly `budget_s` seconds; returns TFLOP/s (float64 arithmetic)."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    M, N, K = a_bits.shape[0], w.n, w.k
+    if w.mode == "tensorwise":
+        qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
+    else:
+        qb, sb = oracle.quantize_groups(b_bits, "bf16", 128, 128)
+    rows = M
+    runs = []
+    t_start = time.perf_counter()
+    while True:
+        a = a_bits[:rows]
+        t0 = time.perf_counter()
+        if w.mode == "tensorwise":
+            qa, sa = oracle.quantize_per_tensor(a, "bf16")
+            if w.quantize_b_per_call:
+                qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
+            oracle.gemm_tensorwise_ref(qa, sa, qb, sb)
+        else:
+            qa, sa = oracle.quantize_groups(a, "bf16", 1, 128)
+            oracle.gemm_blockwise_ref(qa, sa, qb, sb)
+        dt = time.perf_counter() - t0
+        runs.append(dt)
+        if dt * 3 > budget_s and rows > 1 and len(runs) == 1:
+            rows = max(1, int(rows * budget_s / (3 * dt)))
+            runs = []
+            continue
+        if len(runs) >= 3 or time.perf_counter() - t_start > budget_s:
+            break
+    best = min(runs)
+    flops = 2.0 * rows * N * K
+    return {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle quantize(A[{rows},{K}]) + {w.mode} GEMM with W[{N},{K}], best of "
+                      f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import fp8_quantized_gemm_amax_amd as fp8
+    from fp8_quantized_gemm_amax_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    M = args.m if args.m is not None else max(w.m_values)
+    N, K = w.n, w.k
+    a_bits, b_bits = wl.make_inputs(args.workload, M)
+    out_dtype = torch.float16 if w.out_dtype == "f16" else torch.bfloat16
+    blockwise = w.mode == "blockwise"
+
+    a0 = wl.bits_to_tensor(a_bits, device=dev)
+    b0 = wl.bits_to_tensor(b_bits, device=dev)
+    if blockwise:
+        qb0, sb0 = fp8.fp8_quantize_per_token_group(b0, 128, 128)
+    else:
+        qb0, sb0 = fp8.fp8_quantize_per_tensor(b0)
+
+    per_set = 2 * M * K + M * K + 2 * M * N + N * K + (2 * N * K if w.quantize_b_per_call else 0)
+    R = max(2, min(256, -(-ROTATION_BYTES // per_set)))
+    sets = []
+    for _ in range(R):
+        s = {"a": a0.clone(), "c": torch.empty((M, N), dtype=out_dtype, device=dev)}
+        if w.quantize_b_per_call:
+            s["b"] = b0.clone()
+        else:
+            s["qb"], s["sb"] = qb0.clone(), sb0.clone()
+        if blockwise:
+            s["qa"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            s["sa"] = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+        else:
+            s["qa"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            s["sa"] = torch.empty((1,), dtype=torch.float32, device=dev)
+            if w.quantize_b_per_call:
+                s["qb"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
+                s["sb"] = torch.empty((1,), dtype=torch.float32, device=dev)
+        sets.append(s)
+    del a0, b0
+
+    def quantize(s):
+        if blockwise:
+            fp8.fp8_quantize_per_token_group(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
+        else:
+            fp8.fp8_quantize_per_tensor(s["a"], q=s["qa"], scale=s["sa"])
+            if w.quantize_b_per_call:
+                fp8.fp8_quantize_per_tensor(s["b"], q=s["qb"], scale=s["sb"])
+
+    def gemm(s):
+        if blockwise:
+            fp8.fp8_gemm_scaled_blockwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
+        else:
+            fp8.fp8_gemm_scaled_tensorwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
+
+    def step(s):
+        quantize(s)
+        gemm(s)
+
+    # eager warm-up (first launches, lazy initialisation), then one eager reference output
+    for i in range(max(1, args.warmup)):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    ref_c = sets[0]["c"].clone()
+
+    # HIP graphs: one replay runs `R` steps (one per rotation set); a tail graph runs the
+    # remaining K mod R, so exactly K steps are timed.  A second graph holds the R GEMMs
+    # alone; its replays time the dominant kernel.
+    K_steps = args.steps
+    def capture(n, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(sets[i % R])
+        return g
+    n_full, tail = divmod(K_steps, R)
+    g_full = capture(R, step) if n_full else None
+    g_tail = capture(tail, step) if tail else None
+    g_gemm = capture(R, gemm)
+    for _ in range(2):                      # graph warm-up replays
+        if g_full:
+            g_full.replay()
+        g_gemm.replay()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(n_full):
+        g_full.replay()
+    if g_tail:
+        g_tail.replay()
+    end.record()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K_steps
+
+    # the same steps replayed must reproduce the eager output bit for bit
+    if not torch.equal(sets[0]["c"].view(torch.int16), ref_c.view(torch.int16)):
+        raise RuntimeError("graph replay output differs from the eager step")
+
+    gemm_reps = max(1, -(-K_steps // R))
+    gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gs.record()
+    for _ in range(gemm_reps):
+        g_gemm.replay()
+    ge.record()
+    torch.cuda.synchronize()
+    gemm_ms = gs.elapsed_time(ge) / (gemm_reps * R)
+
+    flops = 2.0 * M * N * K
+    step_bytes, gemm_bytes = algorithmic_bytes(w, M)
+    decode = M <= 16
+    if decode:
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        roof = {"bound": "hbm", "achieved": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K_steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "scaling": w.mode,
+                   "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
+                   "gemm_ms": round(gemm_ms, 6), "host_s": round(host_s, 4),
+                   "step_bytes": step_bytes},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,14 @@
+"""FP8 E4M3 amax / quantize / scaled GEMM for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libfp8amax.so`` (C ABI in include/fp8amax.h);
+the functions below are its Python binding under the same names.  Build the library
+with ``python -m fp8_quantized_gemm_amax_amd.build``.
+"""
+
+from .binding import (Fp8Error, fp8_amax, fp8_quantize_per_tensor, fp8_quantize_per_token_group,
+                      fp8_gemm_scaled_tensorwise, fp8_gemm_scaled_blockwise, fp8_debug_cast_f32,
+                      lib, LIB_PATH)
+
+__all__ = ["Fp8Error", "fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_per_token_group",
+           "fp8_gemm_scaled_tensorwise", "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
+           "lib", "LIB_PATH"]

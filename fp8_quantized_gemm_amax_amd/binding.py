@@ -1,0 +1,208 @@
+"""ctypes binding of libfp8amax.so: the C ABI of include/fp8amax.h with the same names.
+
+Argument marshalling only.  torch supplies device memory (outputs are allocated with
+``torch.empty``) and the current HIP stream; every step of the path runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or fails to
+load, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8amax.so")
+
+FP8_BF16, FP8_F16 = 0, 1
+STATUS_NAMES = {0: "FP8_OK", 1: "FP8_ERR_NULL_POINTER", 2: "FP8_ERR_BAD_SHAPE", 3: "FP8_ERR_BAD_DTYPE",
+                4: "FP8_ERR_MISALIGNED", 5: "FP8_ERR_LAUNCH", 6: "FP8_ERR_TOO_LARGE"}
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SIGNATURES = {
+    "fp8_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "fp8_amax": ([_P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, _P], ctypes.c_int),
+    "fp8_quantize_per_tensor": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_quantize_per_token_group": ([_P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "fp8_gemm_scaled_tensorwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "fp8_gemm_scaled_blockwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
+}
+
+
+class Fp8Error(RuntimeError):
+    """A non-zero fp8_status_t from the library."""
+
+    def __init__(self, fn, code, text):
+        super().__init__(f"{fn}: {text}")
+        self.code = code
+        self.status = STATUS_NAMES.get(code, str(code))
+
+
+def lib():
+    """Load libfp8amax.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fp8_quantized_gemm_amax_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(fn, code):
+    if code != 0:
+        text = lib().fp8_status_string(code).decode()
+        raise Fp8Error(fn, code, text)
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return FP8_BF16
+    if t.dtype == torch.float16:
+        return FP8_F16
+    raise TypeError(f"expected a bfloat16 or float16 tensor, got {t.dtype}")
+
+
+def _out_dt(dtype):
+    if dtype == torch.bfloat16:
+        return FP8_BF16
+    if dtype == torch.float16:
+        return FP8_F16
+    raise TypeError(f"output dtype must be bfloat16 or float16, got {dtype}")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _as_2d(x):
+    if x.dim() != 2:
+        raise ValueError(f"expected a 2-D tensor, got shape {tuple(x.shape)}")
+    return x.contiguous()
+
+
+def _codes(t):
+    """Accept uint8 or float8_e4m3fn code tensors; return a uint8 view."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"FP8 operands must be uint8 or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def fp8_amax(x, block_rows=0, block_cols=0, out=None):
+    """amax per tensor ((0,0) -> shape [1]) or per (1,128) / (128,128) block."""
+    x = _as_2d(x)
+    _need_cuda(x)
+    R, C = x.shape
+    shape = (1,) if (block_rows, block_cols) == (0, 0) else (
+        -(-R // max(block_rows, 1)), -(-C // max(block_cols, 1)))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _need_cuda(out)
+    _check("fp8_amax", lib().fp8_amax(_ptr(x), _dt(x), R, C, block_rows, block_cols,
+                                      ctypes.c_void_p(out.data_ptr()), _stream(x)))
+    return out
+
+
+def fp8_quantize_per_tensor(x, q=None, scale=None):
+    """Returns (q uint8 [R, C], scale float32 [1])."""
+    x = _as_2d(x)
+    _need_cuda(x)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _need_cuda(q, scale)
+    _check("fp8_quantize_per_tensor",
+           lib().fp8_quantize_per_tensor(_ptr(x), _dt(x), R, C, _ptr(q),
+                                         ctypes.c_void_p(scale.data_ptr()), _stream(x)))
+    return q, scale
+
+
+def fp8_quantize_per_token_group(x, group_rows=1, group_cols=128, q=None, scales=None):
+    """Returns (q uint8 [R, C], scales float32 [ceil(R/group_rows), ceil(C/group_cols)])."""
+    x = _as_2d(x)
+    _need_cuda(x)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((-(-R // max(group_rows, 1)), -(-C // max(group_cols, 1))),
+                             dtype=torch.float32, device=x.device)
+    _need_cuda(q, scales)
+    _check("fp8_quantize_per_token_group",
+           lib().fp8_quantize_per_token_group(_ptr(x), _dt(x), R, C, group_rows, group_cols,
+                                              _ptr(q), _ptr(scales), _stream(x)))
+    return q, scales
+
+
+def _gemm(name, qa, sa, qb, sb, out_dtype, out):
+    qa, qb = _codes(_as_2d(qa)), _codes(_as_2d(qb))
+    _need_cuda(qa, qb, sa, sb)
+    M, K = qa.shape
+    N, K2 = qb.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: qa has {K}, qb has {K2}")
+    sa = sa.contiguous()
+    sb = sb.contiguous()
+    if sa.dtype != torch.float32 or sb.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _need_cuda(out)
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, _ptr(out), _out_dt(out.dtype),
+                    _stream(qa)))
+    return out
+
+
+def fp8_gemm_scaled_tensorwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
+    """C [M, N] = (qa @ qb^T) * sa * sb; qa [M, K], qb [N, K] e4m3 codes, sa/sb float32 [1]."""
+    if sa.numel() != 1 or sb.numel() != 1:
+        raise ValueError("tensorwise scales are single float32 values")
+    return _gemm("fp8_gemm_scaled_tensorwise", qa, sa, qb, sb, out_dtype, out)
+
+
+def fp8_gemm_scaled_blockwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
+    """Per 128-wide K slab scales: sa [M, K/128], sb [ceil(N/128), K/128]."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    if K % 128 == 0 and K > 0:
+        if tuple(sa.shape) != (M, K // 128) or tuple(sb.shape) != (-(-N // 128), K // 128):
+            raise ValueError(f"blockwise scales must be [{M}, {K // 128}] and [{-(-N // 128)}, {K // 128}], "
+                             f"got {tuple(sa.shape)} and {tuple(sb.shape)}")
+    return _gemm("fp8_gemm_scaled_blockwise", qa, sa, qb, sb, out_dtype, out)
+
+
+def fp8_debug_cast_f32(v, q=None):
+    """q = e4m3(v) elementwise with the library's device encoder (test hook)."""
+    v = v.contiguous()
+    _need_cuda(v)
+    if v.dtype != torch.float32:
+        raise TypeError("fp8_debug_cast_f32 takes float32")
+    if q is None:
+        q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check("fp8_debug_cast_f32", lib().fp8_debug_cast_f32(_ptr(v), _ptr(q), v.numel(), _stream(v)))
+    return q

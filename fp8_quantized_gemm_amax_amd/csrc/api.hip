@@ -1,0 +1,139 @@
+// api.hip - the C ABI declared in include/fp8amax.h: host-side validation, then kernel
+// launches on the caller's stream.  Validation makes no HIP call, so every error path can
+// be exercised on a machine without a GPU.
+#include "fp8amax.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;   // kernels index rows/cols with int
+constexpr int64_t kMaxElems = int64_t{1} << 40;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool valid_dt(fp8_dtype_t dt) { return dt == FP8_BF16 || dt == FP8_F16; }
+
+fp8_status_t check_2d(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return FP8_ERR_BAD_SHAPE;
+  if (rows > kMaxDim || cols > kMaxDim) return FP8_ERR_TOO_LARGE;
+  if (cols > 0 && rows > kMaxElems / cols) return FP8_ERR_TOO_LARGE;
+  return FP8_OK;
+}
+
+bool group_shape_ok(int32_t gr, int32_t gc) { return gc == 128 && (gr == 1 || gr == 128); }
+
+fp8_status_t finish_launch() {
+  return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH;
+}
+
+fp8_status_t gemm_common(bool blockwise, const uint8_t* qa, const float* sa, const uint8_t* qb,
+                         const float* sb, int64_t M, int64_t N, int64_t K, void* c,
+                         fp8_dtype_t out_dt, void* stream) {
+  if (M < 0 || N < 0 || K <= 0) return FP8_ERR_BAD_SHAPE;
+  if (blockwise ? (K % 128 != 0) : (K % 16 != 0)) return FP8_ERR_BAD_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8_ERR_TOO_LARGE;
+  if (!valid_dt(out_dt)) return FP8_ERR_BAD_DTYPE;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!qa || !sa || !qb || !sb || !c) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(qa) || !aligned16(qb) || !aligned16(c) || !aligned4(sa) || !aligned4(sb))
+    return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();   // clear a stale error so FP8_ERR_LAUNCH reports this call only
+  fp8amax::launch_gemm(blockwise, static_cast<int>(out_dt), qa, sa, qb, sb, static_cast<int>(M),
+                       static_cast<int>(N), static_cast<int>(K), c,
+                       static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status_t s) {
+  switch (s) {
+    case FP8_OK: return "FP8_OK";
+    case FP8_ERR_NULL_POINTER: return "FP8_ERR_NULL_POINTER: a required pointer is NULL";
+    case FP8_ERR_BAD_SHAPE: return "FP8_ERR_BAD_SHAPE: unsupported size or group/block shape";
+    case FP8_ERR_BAD_DTYPE: return "FP8_ERR_BAD_DTYPE: unknown 16-bit dtype";
+    case FP8_ERR_MISALIGNED: return "FP8_ERR_MISALIGNED: data pointers need 16-byte, float pointers 4-byte alignment";
+    case FP8_ERR_LAUNCH: return "FP8_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case FP8_ERR_TOO_LARGE: return "FP8_ERR_TOO_LARGE: a dimension exceeds 2^31-1 or a tensor 2^40 elements";
+  }
+  return "unknown fp8_status_t";
+}
+
+fp8_status_t fp8_amax(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                      int32_t block_rows, int32_t block_cols, float* amax, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  const bool whole = block_rows == 0 && block_cols == 0;
+  if (!whole && !group_shape_ok(block_rows, block_cols)) return FP8_ERR_BAD_SHAPE;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  const int64_t n = rows * cols;
+  if (!whole && n == 0) return FP8_OK;                 // empty grid: nothing to write
+  if (!amax || (n > 0 && !x)) return FP8_ERR_NULL_POINTER;
+  if ((x && !aligned16(x)) || !aligned4(amax)) return FP8_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (whole) fp8amax::launch_tensor_reduce(static_cast<int>(dt), x, n, amax, false, s);
+  else fp8amax::launch_groups(static_cast<int>(dt), x, rows, cols, block_rows, nullptr, amax, false, s);
+  return finish_launch();
+}
+
+fp8_status_t fp8_quantize_per_tensor(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                     uint8_t* q, float* scale, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  const int64_t n = rows * cols;
+  if (!scale || (n > 0 && (!x || !q))) return FP8_ERR_NULL_POINTER;
+  if ((x && !aligned16(x)) || (q && !aligned16(q)) || !aligned4(scale)) return FP8_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  fp8amax::launch_tensor_reduce(static_cast<int>(dt), x, n, scale, true, s);
+  if (n > 0) fp8amax::launch_tensor_cast(static_cast<int>(dt), x, n, scale, q, s);
+  return finish_launch();
+}
+
+fp8_status_t fp8_quantize_per_token_group(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                          int32_t group_rows, int32_t group_cols, uint8_t* q,
+                                          float* scales, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  if (!group_shape_ok(group_rows, group_cols)) return FP8_ERR_BAD_SHAPE;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  if (rows * cols == 0) return FP8_OK;
+  if (!x || !q || !scales) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scales)) return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_groups(static_cast<int>(dt), x, rows, cols, group_rows, q, scales, true,
+                         static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+fp8_status_t fp8_gemm_scaled_tensorwise(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                        const float* sb, int64_t M, int64_t N, int64_t K, void* c,
+                                        fp8_dtype_t out_dt, void* stream) {
+  return gemm_common(false, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
+}
+
+fp8_status_t fp8_gemm_scaled_blockwise(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                       const float* sb, int64_t M, int64_t N, int64_t K, void* c,
+                                       fp8_dtype_t out_dt, void* stream) {
+  return gemm_common(true, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
+}
+
+fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* stream) {
+  if (n < 0) return FP8_ERR_BAD_SHAPE;
+  if (n > kMaxElems) return FP8_ERR_TOO_LARGE;
+  if (n == 0) return FP8_OK;
+  if (!v || !q) return FP8_ERR_NULL_POINTER;
+  if (!aligned4(v)) return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_debug_cast(v, n, q, static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+}  // extern "C"

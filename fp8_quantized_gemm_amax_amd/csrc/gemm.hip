@@ -1,0 +1,261 @@
+// gemm.hip - FP8 x FP8 GEMM with float32 accumulation and a scale epilogue, for gfx950.
+//
+// C[m, n] = out( sum_k qa[m, k] * qb[n, k] * scale ), A = qa [M, K], B = qb [N, K], both
+// K-contiguous (C = A @ B^T).
+//   tensorwise: scale = sa * sb, applied once to the float32 accumulator (Transformer
+//     Engine page "Что такое FP8 инференс на H100 (Transformer Engine)?", section 3 steps
+//     5-6 and the pseudocode);
+//   blockwise: each 128-wide K slab g has its own sa[m, g] * sb[n / 128, g] ("FP8 chi
+//     tiết", opening bullets), applied in registers to that slab's float32 partial sum.
+//
+// Design (CDNA4): a workgroup of 4 waves computes a BM x BN tile.  Each K step is one
+// 128-byte slab: the A and B slabs are staged global -> VGPR -> LDS with a double buffer
+// (the next slab's global loads are in flight while the current slab is multiplied), and
+// each wave runs v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales, i.e. a plain FP8
+// product) on 16x16 output sub-tiles.  One 16x16x128 MFMA covers exactly one slab, so the
+// blockwise epilogue is one FMA per accumulator per slab.
+//
+// LDS layout: a slab tile is [rows][128 B]; the 16-byte chunk c of row r is stored at
+// chunk position c ^ (r & 7), so the 16 lanes reading one chunk column of 16 consecutive
+// rows hit distinct banks.
+//
+// MFMA operand roles: the first operand is the B (weight) sub-tile, the second the A
+// sub-tile, so lane l holds C[m = l % 16][n = 4 * (l / 16) + r] for r = 0..3: four
+// consecutive output columns, stored as one 8-byte write.  Each lane supplies the same
+// 32-byte K quarter of its row for both operands, so the product is independent of the
+// order in which the hardware walks K inside the instruction.
+#include "fp8_device.hpp"
+#include "launch.hpp"
+
+namespace fp8amax {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kSlab = 128;
+
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  // cbsz = blgp = 0: both operands e4m3; E8M0 scale 127 = 2^0 on both.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                     // nearest even
+}
+
+template <int OUT>
+__device__ __forceinline__ uint32_t f32_to_out_bits(float f) {
+  if constexpr (OUT == DT_BF16) {
+    return f32_to_bf16_bits(f);
+  } else {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool BLOCKWISE, int OUT>
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m) {
+  constexpr int WAVES_N = BN / WN;
+  constexpr int WAVES_M = BM / WM;
+  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(!BLOCKWISE || (WN <= 128 && 128 % WN == 0), "a wave's columns share one weight block");
+  constexpr int TM = WM / 16;
+  constexpr int TN = WN / 16;
+  constexpr int A_IT = (BM * 8 + kThreads - 1) / kThreads;   // 16-byte chunks per thread
+  constexpr int B_IT = (BN * 8 + kThreads - 1) / kThreads;
+  constexpr int STAGE = (BM + BN) * kSlab;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  const int tile = blockIdx.x;
+  const int tm = tile % tiles_m;
+  const int tn = tile / tiles_m;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int wm = w / WAVES_N;
+  const int wn = w % WAVES_N;
+  const int r16 = lane & 15;
+  const int kq = lane >> 4;      // 32-byte quarter of the slab this lane feeds to the MFMA
+  const int KG = K / kSlab;      // blockwise only (K % 128 == 0 there)
+
+  uint4 ra[A_IT], rb[B_IT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < A_IT; ++j) {
+      const int id = t + kThreads * j;
+      const int row = id >> 3, ch = id & 7;
+      const int gm = m0 + row, kk = k0 + ch * 16;
+      ra[j] = make_uint4(0u, 0u, 0u, 0u);
+      if ((BM * 8 % kThreads == 0 || id < BM * 8) && gm < M && kk < K)
+        ra[j] = *reinterpret_cast<const uint4*>(qa + static_cast<int64_t>(gm) * K + kk);
+    }
+#pragma unroll
+    for (int j = 0; j < B_IT; ++j) {
+      const int id = t + kThreads * j;
+      const int row = id >> 3, ch = id & 7;
+      const int gn = n0 + row, kk = k0 + ch * 16;
+      rb[j] = make_uint4(0u, 0u, 0u, 0u);
+      if ((BN * 8 % kThreads == 0 || id < BN * 8) && gn < N && kk < K)
+        rb[j] = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(gn) * K + kk);
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint8_t* As = lds + stage * STAGE;
+    uint8_t* Bs = As + BM * kSlab;
+#pragma unroll
+    for (int j = 0; j < A_IT; ++j) {
+      const int id = t + kThreads * j;
+      if (BM * 8 % kThreads == 0 || id < BM * 8) {
+        const int row = id >> 3, ch = id & 7;
+        *reinterpret_cast<uint4*>(As + row * kSlab + ((ch ^ (row & 7)) << 4)) = ra[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B_IT; ++j) {
+      const int id = t + kThreads * j;
+      if (BN * 8 % kThreads == 0 || id < BN * 8) {
+        const int row = id >> 3, ch = id & 7;
+        *reinterpret_cast<uint4*>(Bs + row * kSlab + ((ch ^ (row & 7)) << 4)) = rb[j];
+      }
+    }
+  };
+  auto frag = [&](const uint8_t* base, int row) -> v8i {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kSlab + (((2 * kq) ^ (row & 7)) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kSlab + (((2 * kq + 1) ^ (row & 7)) << 4));
+    v8i f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+  };
+
+  // blockwise scales: sa for this lane's row in each M sub-tile, sb for the wave's block
+  const int wave_n0 = n0 + wn * WN;
+  const int nb = wave_n0 / kSlab;
+  const int NB = (N + kSlab - 1) / kSlab;
+  auto load_scales = [&](int g, float* out) {
+    const float sbv = (nb < NB) ? sb[static_cast<int64_t>(nb) * KG + g] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm * WM + 16 * i + r16;
+      out[i] = (m < M) ? sa[static_cast<int64_t>(m) * KG + g] * sbv : 0.0f;
+    }
+  };
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  float scl[TM], scl_next[TM];
+  if constexpr (BLOCKWISE) load_scales(0, scl);
+
+  const int nslabs = (K + kSlab - 1) / kSlab;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nslabs; ++s) {
+    const int cur = s & 1;
+    const bool more = s + 1 < nslabs;
+    if (more) gload((s + 1) * kSlab);
+    if constexpr (BLOCKWISE) {
+      if (more) load_scales(s + 1, scl_next);
+    }
+    const uint8_t* As = lds + cur * STAGE;
+    const uint8_t* Bs = As + BM * kSlab;
+    v8i af[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = frag(As, wm * WM + 16 * i + r16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const v8i bf = frag(Bs, wn * WN + 16 * j + r16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (BLOCKWISE) {
+          const v4f p = mfma_fp8(bf, af[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], scl[i], acc[i][j][r]);
+        } else {
+          acc[i][j] = mfma_fp8(bf, af[i], acc[i][j]);
+        }
+      }
+    }
+    if (more) lstore(cur ^ 1);
+    if constexpr (BLOCKWISE) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) scl[i] = scl_next[i];
+    }
+    __syncthreads();
+  }
+
+  float alpha = 1.0f;
+  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  const bool vec_store = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WM + 16 * i + r16;
+    if (m >= M) continue;
+    uint16_t* crow = c + static_cast<int64_t>(m) * N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = wave_n0 + 16 * j + 4 * kq;
+      uint32_t h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * alpha);
+      if (vec_store && n + 3 < N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool BW, int OUT>
+void launch_cfg(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+                int K, void* c, hipStream_t s) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  gemm_fp8_kernel<BM, BN, WM, WN, BW, OUT><<<tiles_m * tiles_n, kThreads, 0, s>>>(
+      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m);
+}
+
+template <bool BW, int OUT>
+void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+                   int K, void* c, hipStream_t s) {
+  const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + (BW ? 127 : 255)) / (BW ? 128 : 256));
+  if (M <= 16) {
+    launch_cfg<16, 256, 16, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+  } else if (big_tiles >= 512) {
+    if constexpr (BW) launch_cfg<256, 128, 128, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_cfg<256, 256, 128, 128, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+  } else {
+    launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+  }
+}
+
+}  // namespace
+
+void launch_gemm(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
+                 const float* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (blockwise) {
+    if (out_dt == DT_BF16) launch_gemm_t<true, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_gemm_t<true, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
+  } else {
+    if (out_dt == DT_BF16) launch_gemm_t<false, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_gemm_t<false, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
+  }
+}
+
+}  // namespace fp8amax

@@ -1,0 +1,389 @@
+// quantize.hip - amax, scale and e4m3 cast kernels for gfx950.
+//
+// Steps (Transformer Engine page "Что такое FP8 инференс на H100 (Transformer Engine)?",
+// section 3 steps 2-4): amax of the operand, scale = amax / 448, x / scale rounded to
+// e4m3.  Block shapes ("FP8 chi tiết", opening bullets): per token in groups of 128 input
+// channels, and 128x128 weight blocks.
+//
+// All kernels are HBM-bound streaming passes: 16-byte loads of eight 16-bit inputs per
+// lane, 8-byte stores of eight codes.  For groups and blocks the amax, scale and cast are
+// fused in one pass that keeps the block's inputs in registers between the reduction and
+// the cast.
+#include "fp8_device.hpp"
+#include "launch.hpp"
+
+namespace fp8amax {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 load16(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return {v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ uint32_t key8(const U4& v) {
+  uint32_t m = key_max_pair(0u, v.x);
+  m = key_max_pair(m, v.y);
+  m = key_max_pair(m, v.z);
+  return key_max_pair(m, v.w);
+}
+
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) { return in_to_f32<DT>(w & 0xffffu); }
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) { return in_to_f32<DT>(w >> 16); }
+
+// Exact path: IEEE division and the software encoder, element by element.  Used for
+// groups whose scale is NaN, infinite or below 2^-100.
+template <int DT>
+__device__ __forceinline__ uint32_t enc4_exact(uint32_t w0, uint32_t w1, float s) {
+  return e4m3_encode(lo16<DT>(w0) / s) | (e4m3_encode(hi16<DT>(w0) / s) << 8) |
+         (e4m3_encode(lo16<DT>(w1) / s) << 16) | (e4m3_encode(hi16<DT>(w1) / s) << 24);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t enc4_fast(uint32_t w0, uint32_t w1, float s, float r) {
+  return cvt4(quot_fast(lo16<DT>(w0), s, r), quot_fast(hi16<DT>(w0), s, r),
+              quot_fast(lo16<DT>(w1), s, r), quot_fast(hi16<DT>(w1), s, r));
+}
+
+// Eight 16-bit inputs -> eight e4m3 codes.  `fast` = fast_scale(s), r = 1/s.
+template <int DT>
+__device__ __forceinline__ uint2 enc8(const U4& v, float s, float r, bool fast) {
+  if (fast) return make_uint2(enc4_fast<DT>(v.x, v.y, s, r), enc4_fast<DT>(v.z, v.w, s, r));
+  return make_uint2(enc4_exact<DT>(v.x, v.y, s), enc4_exact<DT>(v.z, v.w, s));
+}
+
+// One element (ragged paths).
+template <int DT>
+__device__ __forceinline__ uint8_t enc1(uint32_t h, float s, float r, bool fast) {
+  const float x = in_to_f32<DT>(h);
+  if (fast) {
+    const float q = quot_fast(x, s, r);
+    return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xff);
+  }
+  return static_cast<uint8_t>(e4m3_encode(x / s));
+}
+
+// ------------------------------------------------------------------------------------
+// Per-token 1x128 groups.  Sixteen lanes (one DPP row) own one group, 8 elements each.
+// Each 16-lane set takes one (row, chunk) pair: `cg` consecutive groups of one row,
+// walked kUnroll groups at a time with all loads issued before the reductions.
+// Vector path: cols % 8 == 0 (a lane's eight elements are all inside or all outside).
+// WRITE_Q = false computes only the amax grid (fp8_amax with 1x128 blocks).
+constexpr int kUnroll = 2;
+
+template <int DT, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t nch, int64_t cg,
+    uint8_t* __restrict__ q, float* __restrict__ out) {
+  const int64_t gcols = (cols + 127) >> 7;
+  const int sub = threadIdx.x & 15;
+  const int64_t nsets = rows * nch;
+  const int64_t set_stride = (static_cast<int64_t>(gridDim.x) * kThreads) >> 4;
+  for (int64_t set = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 4; set < nsets;
+       set += set_stride) {                        // whole 16-lane sets iterate together
+  const int64_t row = set / nch;
+  const int64_t g_begin = (set - row * nch) * cg;
+  const int64_t g_end = min(g_begin + cg, gcols);
+  const uint16_t* xrow = x + row * cols;
+  for (int64_t g0 = g_begin; g0 < g_end; g0 += kUnroll) {
+    U4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t col = ((g0 + u) << 7) + (sub << 3);
+      v[u] = {0u, 0u, 0u, 0u};
+      if (g0 + u < g_end && col < cols) v[u] = load16(xrow + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = g0 + u;
+      if (g >= g_end) break;                       // uniform within the set
+      const int64_t col = (g << 7) + (sub << 3);
+      const uint32_t key = max16(key8(v[u]));
+      const float amax = amax_from_key<DT>(key);
+      if constexpr (WRITE_Q) {
+        const float scale = scale_from_amax(amax);
+        const bool fast = fast_scale(scale);
+        const float r = 1.0f / scale;
+        if (col < cols) *reinterpret_cast<uint2*>(q + row * cols + col) = enc8<DT>(v[u], scale, r, fast);
+        if (sub == 0) out[row * gcols + g] = scale;
+      } else {
+        if (sub == 0) out[row * gcols + g] = amax;
+      }
+    }
+  }
+  }
+}
+
+// Scalar path for rows whose length is not a multiple of 8: one group per 16-lane set.
+template <int DT, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads) void group_1x128_scalar_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+    float* __restrict__ out) {
+  const int64_t gcols = (cols + 127) >> 7;
+  const int64_t ngroups = rows * gcols;
+  const int sub = threadIdx.x & 15;
+  const int64_t g_stride = (static_cast<int64_t>(gridDim.x) * kThreads) >> 4;
+  for (int64_t g = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 4; g < ngroups;
+       g += g_stride) {
+  const int64_t row = g / gcols;
+  const int64_t gc = g - row * gcols;
+  const int64_t col0 = (gc << 7) + (sub << 3);
+  uint32_t h[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = (col0 + i < cols) ? x[row * cols + col0 + i] : 0u;
+    m = max(m, h[i] & 0x7fffu);
+  }
+  const uint32_t key = max16(m);
+  const float amax = amax_from_key<DT>(key);
+  if constexpr (WRITE_Q) {
+    const float scale = scale_from_amax(amax);
+    const bool fast = fast_scale(scale);
+    const float r = 1.0f / scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (col0 + i < cols) q[row * cols + col0 + i] = enc1<DT>(h[i], scale, r, fast);
+    if (sub == 0) out[g] = scale;
+  } else {
+    if (sub == 0) out[g] = amax;
+  }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// 128x128 weight blocks: one workgroup per block.  Thread t owns columns
+// [8*(t%16), +8) of rows t/16 + 16*i, i = 0..7: eight 16-byte loads held in registers
+// through the block-wide reduction, then cast and stored.  VEC: cols % 8 == 0.
+template <int DT, bool WRITE_Q, bool VEC>
+__global__ __launch_bounds__(kThreads) void block_128x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+    float* __restrict__ out) {
+  __shared__ uint32_t wave_max[kThreads / 64];
+  const int64_t bcols = (cols + 127) >> 7;
+  const int64_t nblocks = ((rows + 127) >> 7) * bcols;
+  const int t = threadIdx.x;
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+  const int64_t br = blk / bcols;
+  const int64_t bc = blk - br * bcols;
+  const int64_t col = (bc << 7) + ((t & 15) << 3);
+  const int64_t row0 = (br << 7) + (t >> 4);
+  U4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = row0 + 16 * i;
+    v[i] = {0u, 0u, 0u, 0u};
+    if constexpr (VEC) {
+      if (row < rows && col < cols) v[i] = load16(x + row * cols + col);
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = (row < rows && col + e < cols) ? x[row * cols + col + e] : 0u;
+      v[i] = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+    m = max(m, key8(v[i]));
+  }
+  m = max64(m);
+  if ((t & 63) == 0) wave_max[t >> 6] = m;
+  __syncthreads();
+  m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+  __syncthreads();                                 // wave_max is rewritten next iteration
+  const float amax = amax_from_key<DT>(m);
+  if constexpr (WRITE_Q) {
+    const float scale = scale_from_amax(amax);
+    const bool fast = fast_scale(scale);
+    const float r = 1.0f / scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = row0 + 16 * i;
+      if (row >= rows) continue;
+      const uint2 o = enc8<DT>(v[i], scale, r, fast);
+      if constexpr (VEC) {
+        if (col < cols) *reinterpret_cast<uint2*>(q + row * cols + col) = o;
+      } else {
+        const uint32_t b[2] = {o.x, o.y};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < cols) q[row * cols + col + e] = static_cast<uint8_t>(b[e >> 2] >> (8 * (e & 3)));
+      }
+    }
+    if (t == 0) out[blk] = scale;
+  } else {
+    if (t == 0) out[blk] = amax;
+  }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Whole-tensor amax.  While the reduction runs, the 32-bit result word holds the running
+// max key tagged with the top bit (kKeyTag | key); each workgroup folds its key in with a
+// single atomicMax (no compare-and-swap retries).  Every final value written to the word
+// (amax or amax / 448: non-negative, inf, or the canonical NaN) has the top bit clear, so
+// a reader can always tell a pending key from a finished float (resolve_word).
+constexpr uint32_t kKeyTag = 0x80000000u;
+
+__global__ void init_word_kernel(uint32_t* word) { *word = kKeyTag; }
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tensor_amax_kernel(const uint16_t* __restrict__ x,
+                                                               int64_t n, uint32_t* word) {
+  __shared__ uint32_t wave_max[kThreads / 64];
+  const int64_t nvec = n >> 3;
+  uint32_t m = 0;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  int64_t i = tid;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {   // four loads in flight per lane
+    const U4 v0 = load16(x + (i << 3)), v1 = load16(x + ((i + stride) << 3));
+    const U4 v2 = load16(x + ((i + 2 * stride) << 3)), v3 = load16(x + ((i + 3 * stride) << 3));
+    m = max(max(m, max(key8(v0), key8(v1))), max(key8(v2), key8(v3)));
+  }
+  for (; i < nvec; i += stride) m = max(m, key8(load16(x + (i << 3))));
+  for (int64_t j = (nvec << 3) + tid; j < n; j += stride) m = max(m, x[j] & 0x7fffu);
+  m = max64(m);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    atomicMax(word, kKeyTag | m);
+  }
+}
+
+// The float a result word stands for: a pending key is turned into amax (or its scale).
+template <int DT, bool WANT_SCALE>
+__device__ __forceinline__ float resolve_word(uint32_t w) {
+  if (!(w & kKeyTag)) return __uint_as_float(w);
+  const float amax = amax_from_key<DT>(w & 0x7fffu);
+  return WANT_SCALE ? scale_from_amax(amax) : amax;
+}
+
+template <int DT, bool WANT_SCALE>
+__global__ void finalize_word_kernel(uint32_t* word) {
+  *word = __float_as_uint(resolve_word<DT, WANT_SCALE>(*word));
+}
+
+// Cast with the per-tensor scale.  Every workgroup resolves the word itself (pending key or finished float give the same
+// scale) and writes the finished float back; the writes all carry the same value.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tensor_cast_kernel(const uint16_t* __restrict__ x,
+                                                               int64_t n, uint32_t* word,
+                                                               uint8_t* __restrict__ q) {
+  const float scale = resolve_word<DT, true>(*word);
+  if (threadIdx.x == 0) *word = __float_as_uint(scale);
+  const bool fast = fast_scale(scale);
+  const float r = 1.0f / scale;
+  const int64_t nvec = n >> 3;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  int64_t i = tid;
+  for (; i + stride < nvec; i += 2 * stride) {      // two loads in flight per lane
+    const U4 v0 = load16(x + (i << 3));
+    const U4 v1 = load16(x + ((i + stride) << 3));
+    *reinterpret_cast<uint2*>(q + (i << 3)) = enc8<DT>(v0, scale, r, fast);
+    *reinterpret_cast<uint2*>(q + ((i + stride) << 3)) = enc8<DT>(v1, scale, r, fast);
+  }
+  if (i < nvec) *reinterpret_cast<uint2*>(q + (i << 3)) = enc8<DT>(load16(x + (i << 3)), scale, r, fast);
+  for (int64_t j = (nvec << 3) + tid; j < n; j += stride) q[j] = enc1<DT>(x[j], scale, r, fast);
+}
+
+__global__ __launch_bounds__(kThreads) void debug_cast_kernel(const float* __restrict__ v, int64_t n,
+                                                              uint8_t* __restrict__ q) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = tid; i < n; i += stride) q[i] = static_cast<uint8_t>(e4m3_encode(v[i]));
+}
+
+inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return static_cast<unsigned>(g);
+}
+
+constexpr int64_t kStreamCap = 256 * 16;     // 16 workgroups per CU on 256 CUs
+constexpr int64_t kReduceCap = 256 * 4;      // whole-tensor reduction workgroups
+constexpr int64_t kGroupCap = 256 * 256;     // group/block kernels loop beyond this grid
+
+template <int DT>
+void launch_groups_t(const void* x, int64_t rows, int64_t cols, int32_t group_rows, uint8_t* q,
+                     float* out, bool write_q, hipStream_t s) {
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const bool vec = (cols % 8) == 0;
+  if (group_rows == 1) {
+    const int64_t gcols = (cols + 127) / 128;
+    const int64_t ngroups = rows * gcols;
+    if (vec) {
+      // aim for ~16k 16-lane sets (16 waves per CU); each takes cg consecutive groups
+      constexpr int64_t kTargetSets = 256 * 64;
+      int64_t cg = (ngroups + kTargetSets - 1) / kTargetSets;
+      cg = ((cg + kUnroll - 1) / kUnroll) * kUnroll;
+      const int64_t nch = (gcols + cg - 1) / cg;
+      const unsigned grid = grid_for(rows * nch, 16, kGroupCap);
+      if (write_q) group_1x128_vec_kernel<DT, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out);
+      else group_1x128_vec_kernel<DT, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out);
+    } else {
+      const unsigned grid = grid_for(ngroups, 16, kGroupCap);
+      if (write_q) group_1x128_scalar_kernel<DT, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+      else group_1x128_scalar_kernel<DT, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+    }
+  } else {
+    const unsigned grid = grid_for(((rows + 127) / 128) * ((cols + 127) / 128), 1, kGroupCap);
+    if (vec) {
+      if (write_q) block_128x128_kernel<DT, true, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+      else block_128x128_kernel<DT, false, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+    } else {
+      if (write_q) block_128x128_kernel<DT, true, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+      else block_128x128_kernel<DT, false, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+    }
+  }
+}
+
+template <int DT>
+void launch_tensor_reduce_t(const void* x, int64_t n, float* word, bool want_scale, hipStream_t s) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(word);
+  init_word_kernel<<<1, 1, 0, s>>>(w);
+  const unsigned grid = grid_for(n, kThreads * 8 * 4, kReduceCap);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  tensor_amax_kernel<DT><<<grid, kThreads, 0, s>>>(xp, n, w);
+  // the cast kernel finishes a scale word itself; otherwise convert it here
+  if (!want_scale) finalize_word_kernel<DT, false><<<1, 1, 0, s>>>(w);
+  else if (n == 0) finalize_word_kernel<DT, true><<<1, 1, 0, s>>>(w);
+}
+
+}  // namespace
+
+void launch_groups(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
+                   uint8_t* q, float* out, bool write_q, hipStream_t s) {
+  if (dt == DT_BF16) launch_groups_t<DT_BF16>(x, rows, cols, group_rows, q, out, write_q, s);
+  else launch_groups_t<DT_F16>(x, rows, cols, group_rows, q, out, write_q, s);
+}
+
+void launch_tensor_reduce(int dt, const void* x, int64_t n, float* word, bool want_scale,
+                          hipStream_t s) {
+  if (dt == DT_BF16) launch_tensor_reduce_t<DT_BF16>(x, n, word, want_scale, s);
+  else launch_tensor_reduce_t<DT_F16>(x, n, word, want_scale, s);
+}
+
+void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t* q,
+                        hipStream_t s) {
+  const unsigned grid = grid_for(n, kThreads * 8, kStreamCap);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint32_t* w = reinterpret_cast<uint32_t*>(scale);
+  if (dt == DT_BF16) tensor_cast_kernel<DT_BF16><<<grid, kThreads, 0, s>>>(xp, n, w, q);
+  else tensor_cast_kernel<DT_F16><<<grid, kThreads, 0, s>>>(xp, n, w, q);
+}
+
+void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s) {
+  const unsigned grid = grid_for(n, kThreads, kStreamCap);
+  debug_cast_kernel<<<grid, kThreads, 0, s>>>(v, n, q);
+}
+
+}  // namespace fp8amax

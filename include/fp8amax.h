@@ -1,0 +1,151 @@
+/*
+ * fp8amax.h - C ABI of the MI355X (gfx950) FP8 E4M3 amax / quantize / scaled-GEMM library.
+ *
+ * The operation, as the pages describe it:
+ *   - "Что такое FP8 инференс на H100 (Transformer Engine)?", section 3 (steps 2-6 and
+ *     the pseudocode): before each GEMM take the largest magnitude (amax) of each
+ *     operand, scale = amax / 448 (448 is the largest E4M3 value), divide the operand
+ *     by its scale and round to FP8, multiply the FP8 operands with a float32
+ *     accumulator, and multiply the result by scale_A * scale_B before the 16-bit
+ *     output.
+ *   - "FP8 chi tiết" (Transformers fine-grained FP8 page), opening bullets: weights are
+ *     quantized per 128x128 block and activations per token in groups of 128 input
+ *     channels, so blockwise scales change every 128 input channels.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller (PyTorch tensors in
+ *     practice).  The library allocates nothing and keeps no state between calls.
+ *   - Tensors are dense and row-major: the last index is contiguous and the leading
+ *     dimension equals the column count.  A is [M, K], B (weights) is [N, K] and the
+ *     product is C = A @ B^T, [M, N].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All work
+ *     is enqueued on it and the call returns without waiting; device faults surface
+ *     at the caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call.  A non-zero status
+ *     means nothing was launched (except FP8_ERR_LAUNCH, which reports a failed
+ *     launch); outputs are then unspecified.
+ *   - Empty inputs (a zero dimension) are valid; see each entry point.
+ *   - Data pointers (x, q, qa, qb, c) must be 16-byte aligned and float32 pointers
+ *     (scales, amax) 4-byte aligned (FP8_ERR_MISALIGNED otherwise).
+ *   - FP8 bytes are OCP "e4m3fn" codes: 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ *     largest finite 448, S.1111.111 = NaN, no infinities.
+ *
+ * Rules the pages leave open (the same in every entry point):
+ *   - scale = amax / 448 is one IEEE float32 division (round to nearest even, subnormal
+ *     results kept); an amax of 0 gives scale 1.0; NaN or inf propagate.
+ *   - q = e4m3(x / scale): one IEEE float32 division per element, then round to
+ *     nearest even with saturation at +-448 (inf included); NaN gives 0x7F; the sign
+ *     of zero and of values that round to zero is kept.
+ *   - amax propagates NaN (a NaN anywhere in a block makes that block's amax NaN);
+ *     a NaN amax or scale is always the canonical quiet NaN 0x7FC00000.
+ */
+#ifndef FP8AMAX_H
+#define FP8AMAX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  FP8_ERR_BAD_SHAPE = 2,    /* negative size, unsupported group/block shape, K rule broken */
+  FP8_ERR_BAD_DTYPE = 3,    /* unknown fp8_dtype_t value */
+  FP8_ERR_MISALIGNED = 4,   /* a base pointer is not 16-byte aligned */
+  FP8_ERR_LAUNCH = 5,       /* the HIP runtime reported an error for a launch */
+  FP8_ERR_TOO_LARGE = 6     /* a size exceeds what the kernels index (elements >= 2^40) */
+} fp8_status_t;
+
+/* 16-bit floating point types used for inputs (activations, weights) and outputs. */
+typedef enum { FP8_BF16 = 0, FP8_F16 = 1 } fp8_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8_status_string(fp8_status_t s);
+
+/*
+ * fp8_amax - largest magnitude per tensor or per block (Transformer Engine page,
+ * section 3 step 2; block shapes from "FP8 chi tiết", opening bullets).
+ *   x      : [rows, cols] of `dt` (bf16 or fp16).
+ *   block_rows, block_cols : (0, 0) for one value over the whole tensor;
+ *            (1, 128) for per-token groups of 128 columns; (128, 128) for weight blocks.
+ *   amax   : float32 output, [ceil(rows/block_rows), ceil(cols/block_cols)] row-major,
+ *            or [1] for the whole tensor.  Blocks on a ragged edge cover only the
+ *            elements that exist.  An empty tensor gives 0 (whole-tensor mode) or an
+ *            empty grid (nothing written).
+ * Errors: NULL x or amax (when there is anything to write), negative sizes, other
+ * block shapes, misaligned pointers, unknown dtype.
+ */
+fp8_status_t fp8_amax(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                      int32_t block_rows, int32_t block_cols, float* amax, void* stream);
+
+/*
+ * fp8_quantize_per_tensor - one scale for the whole tensor (Transformer Engine page,
+ * section 3 steps 2-4 and the pseudocode).
+ *   x     : [rows, cols] of `dt`.
+ *   q     : uint8 output [rows, cols], e4m3fn codes of x / scale.
+ *   scale : float32 output [1], amax / 448 (1.0 for an all-zero or empty tensor).
+ *           The same word also serves as the reduction's scratch while the call runs,
+ *           so it must not alias x or q.
+ * Errors: as fp8_amax.
+ */
+fp8_status_t fp8_quantize_per_tensor(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                     uint8_t* q, float* scale, void* stream);
+
+/*
+ * fp8_quantize_per_token_group - blockwise scales with amax, scale and cast fused in
+ * one pass over x ("FP8 chi tiết", opening bullets).
+ *   group_rows, group_cols : (1, 128) per-token activation groups, or (128, 128)
+ *            weight blocks.  Other shapes give FP8_ERR_BAD_SHAPE.
+ *   x      : [rows, cols] of `dt`.
+ *   q      : uint8 output [rows, cols].
+ *   scales : float32 output [ceil(rows/group_rows), ceil(cols/group_cols)] row-major.
+ * Errors: as fp8_amax.
+ */
+fp8_status_t fp8_quantize_per_token_group(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                          int32_t group_rows, int32_t group_cols,
+                                          uint8_t* q, float* scales, void* stream);
+
+/*
+ * fp8_gemm_scaled_tensorwise - C = out( (sum_k qa[m,k] * qb[n,k]) * sa * sb )
+ * (Transformer Engine page, section 3 steps 5-6 and the pseudocode).
+ *   qa : uint8 e4m3fn [M, K];  sa : float32 [1] (device)
+ *   qb : uint8 e4m3fn [N, K];  sb : float32 [1] (device)
+ *   c  : [M, N] of out_dt (bf16 or fp16), rounded to nearest even.
+ * Products are accumulated in float32 on the gfx950 FP8 matrix cores.
+ * Requires K % 16 == 0 (the task page pads hidden sizes to a multiple of 16) and K > 0.
+ * M == 0 or N == 0 returns FP8_OK with nothing launched.
+ */
+fp8_status_t fp8_gemm_scaled_tensorwise(const uint8_t* qa, const float* sa,
+                                        const uint8_t* qb, const float* sb,
+                                        int64_t M, int64_t N, int64_t K,
+                                        void* c, fp8_dtype_t out_dt, void* stream);
+
+/*
+ * fp8_gemm_scaled_blockwise - per 128-wide K slab g:
+ *   C = out( sum_g sa[m, g] * sb[n / 128, g] * (sum_{k in slab g} qa[m,k] * qb[n,k]) )
+ * ("FP8 chi tiết", opening bullets: 1x128 activation groups, 128x128 weight blocks).
+ *   qa : uint8 e4m3fn [M, K];  sa : float32 [M, K/128]
+ *   qb : uint8 e4m3fn [N, K];  sb : float32 [ceil(N/128), K/128]
+ *   c  : [M, N] of out_dt.
+ * Each slab's partial sum is float32 and is scaled in registers before it is added.
+ * Requires K % 128 == 0 and K > 0.  M == 0 or N == 0 returns FP8_OK.
+ */
+fp8_status_t fp8_gemm_scaled_blockwise(const uint8_t* qa, const float* sa,
+                                       const uint8_t* qb, const float* sb,
+                                       int64_t M, int64_t N, int64_t K,
+                                       void* c, fp8_dtype_t out_dt, void* stream);
+
+/*
+ * fp8_debug_cast_f32 - test hook: q[i] = e4m3(v[i]) with the same device encoder the
+ * quantizers use (saturating round to nearest even; NaN -> 0x7F).  v is float32 [n],
+ * q is uint8 [n].  n == 0 returns FP8_OK.
+ */
+fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8AMAX_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every function include/fp8amax.h declares, and
+rejects bad arguments with the documented status codes before any HIP call (so these
+run on a machine without a GPU: no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_quantized_gemm_amax_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULLP, SHAPE, DTYPE, ALIGN, LAUNCH, LARGE = range(7)
+A16 = 0x10000          # fake, 16-byte aligned addresses (never dereferenced: validation fails first)
+MIS = 0x10001
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fp8amax.h")).read()
+    return re.findall(r"^(?:fp8_status_t|const char\*)\s+(fp8_\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert set(names) == {"fp8_status_string", "fp8_amax", "fp8_quantize_per_tensor",
+                          "fp8_quantize_per_token_group", "fp8_gemm_scaled_tensorwise",
+                          "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding._SIGNATURES)
+
+
+def test_status_strings(L):
+    for code, name in binding.STATUS_NAMES.items():
+        assert L.fp8_status_string(code).decode().startswith(name)
+    assert L.fp8_status_string(99) == b"unknown fp8_status_t"
+
+
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled_tensorwise", "fp8_gemm_scaled_blockwise"])
+def test_gemm_validation(L, fn):
+    f = getattr(L, fn)
+    good = (A16, A16, A16, A16)
+    assert f(*good, 4, 4, 0, A16, 0, None) == SHAPE          # K == 0
+    assert f(*good, -1, 4, 128, A16, 0, None) == SHAPE
+    assert f(*good, 4, -2, 128, A16, 0, None) == SHAPE
+    assert f(*good, 4, 4, 120 if "blockwise" in fn else 24, A16, 0, None) == SHAPE   # K rule
+    assert f(*good, 4, 4, 128, A16, 7, None) == DTYPE
+    assert f(*good, 0, 4, 128, A16, 0, None) == OK            # empty: nothing launched
+    assert f(*good, 4, 0, 128, A16, 0, None) == OK
+    assert f(None, A16, A16, A16, 4, 4, 128, A16, 0, None) == NULLP
+    assert f(A16, A16, A16, A16, 4, 4, 128, None, 0, None) == NULLP
+    assert f(MIS, A16, A16, A16, 4, 4, 128, A16, 0, None) == ALIGN
+    assert f(A16, A16, A16, A16, 4, 4, 128, MIS, 0, None) == ALIGN
+    assert f(A16, A16 + 2, A16, A16, 4, 4, 128, A16, 0, None) == ALIGN   # float pointer needs 4 B
+    assert f(*good, 2 ** 31, 4, 128, A16, 0, None) == LARGE
+
+
+def test_quantize_validation(L):
+    q = L.fp8_quantize_per_token_group
+    assert q(A16, 0, 4, 256, 2, 128, A16, A16, None) == SHAPE      # unsupported group
+    assert q(A16, 0, 4, 256, 1, 64, A16, A16, None) == SHAPE
+    assert q(A16, 0, -4, 256, 1, 128, A16, A16, None) == SHAPE
+    assert q(A16, 2, 4, 256, 1, 128, A16, A16, None) == DTYPE
+    assert q(A16, 0, 0, 256, 1, 128, None, None, None) == OK        # empty
+    assert q(None, 0, 4, 256, 1, 128, A16, A16, None) == NULLP
+    assert q(MIS, 0, 4, 256, 128, 128, A16, A16, None) == ALIGN
+    assert q(A16, 0, 4, 256, 128, 128, MIS, A16, None) == ALIGN
+    p = L.fp8_quantize_per_tensor
+    assert p(A16, 0, 4, 256, A16, None, None) == NULLP               # scale is always written
+    assert p(A16, 5, 4, 256, A16, A16, None) == DTYPE
+    assert p(A16, 0, 4, -1, A16, A16, None) == SHAPE
+    assert p(A16, 0, 2 ** 31, 2, A16, A16, None) == LARGE
+    assert p(A16, 0, 2 ** 30, 2 ** 30, A16, A16, None) == LARGE      # 2^60 elements
+    a = L.fp8_amax
+    assert a(A16, 0, 4, 256, 1, 64, A16, None) == SHAPE
+    assert a(A16, 0, 4, 256, 0, 128, A16, None) == SHAPE
+    assert a(A16, 0, 0, 256, 1, 128, None, None) == OK               # empty grid
+    assert a(A16, 0, 4, 256, 0, 0, None, None) == NULLP
+    assert a(A16, 0, 4, 256, 0, 0, A16 + 1, None) == ALIGN
+    d = L.fp8_debug_cast_f32
+    assert d(A16, A16, -1, None) == SHAPE
+    assert d(A16, A16, 0, None) == OK
+    assert d(None, A16, 8, None) == NULLP
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import fp8_quantized_gemm_amax_amd as f
+    with pytest.raises(ValueError):
+        f.fp8_quantize_per_token_group(torch.zeros(4, 128, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        f.fp8_gemm_scaled_tensorwise(torch.zeros(4, 128, dtype=torch.float32), torch.ones(1),
+                                     torch.zeros(4, 128, dtype=torch.uint8), torch.ones(1))

@@ -1,0 +1,197 @@
+"""GPU parity for the cast, amax and quantize entry points: bit-exact bytes and scales
+against the CPU oracle, through the C ABI (Python binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_quantized_gemm_amax_amd as fp8
+from fp8_quantized_gemm_amax_amd import workloads as wl
+from parity_util import (DEV, to_dev, guarded_u8, guarded_f32, guard_intact, host_u8, host_f32,
+                         assert_bytes_equal)
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------------------- cast
+
+def test_debug_cast_all_fp32_patterns():
+    """All 2^32 float32 patterns through the device encoder, against the oracle's
+    encoder written as its 126 breakpoints (the code of a non-negative pattern is the
+    number of breakpoints at or below it; NaN -> 0x7F; negative -> 0x80 | code(|p|))."""
+    bp = torch.from_numpy(oracle.nonneg_breakpoints().astype(np.int64)).to(DEV)
+    chunk = 1 << 28
+    total_bad = 0
+    first = None
+    for c in range(16):
+        p0 = c * chunk
+        start = p0 if p0 < 2 ** 31 else p0 - 2 ** 32
+        pats = torch.arange(start, start + chunk, dtype=torch.int32, device=DEV)
+        got = fp8.fp8_debug_cast_f32(pats.view(torch.float32))
+        mag = pats.to(torch.int64) & 0x7FFFFFFF
+        neg = pats < 0
+        code = torch.searchsorted(bp, mag, right=True)
+        want = torch.where(neg, code | 0x80, code)
+        want = torch.where(mag > 0x7F800000, torch.full_like(want, 0x7F), want).to(torch.uint8)
+        bad = got != want
+        nb = int(bad.sum())
+        if nb and first is None:
+            i = int(torch.nonzero(bad)[0])
+            first = (hex((p0 + i) & 0xFFFFFFFF), int(got[i]), int(want[i]))
+        total_bad += nb
+        del pats, got, mag, neg, code, want, bad
+    assert total_bad == 0, f"{total_bad} mismatching patterns; first {first}"
+
+
+# ----------------------------------------------------------------------------- groups
+
+def check_groups(bits, dtype, gr, label):
+    R, C = bits.shape
+    q_want, s_want = oracle.quantize_groups(bits, dtype, gr, 128)
+    x = to_dev(bits, dtype)
+    q, qfull = guarded_u8((R, C))
+    s, sfull = guarded_f32(s_want.shape)
+    fp8.fp8_quantize_per_token_group(x, gr, 128, q=q, scales=s)
+    assert_bytes_equal(host_f32(s), s_want, f"{label} scales")
+    assert_bytes_equal(host_u8(q), q_want, f"{label} codes")
+    assert guard_intact(qfull, R * C, "u8") and guard_intact(sfull, s_want.size, "f32"), label
+    # fp8_amax on the same blocks
+    a = fp8.fp8_amax(x, gr, 128)
+    assert_bytes_equal(host_f32(a), oracle.amax_groups(oracle.input_to_f32(bits, dtype), gr, 128),
+                       f"{label} amax")
+    return q, s
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_mlp_blockwise", "deepseek_v3_blockwise"])
+def test_token_groups_workload_activations(name):
+    a_bits, _ = wl.make_inputs(name)
+    check_groups(a_bits, "bf16", 1, name)
+
+
+def all_patterns(dtype):
+    """Every 16-bit pattern once, in [512, 128]: rows mix NaN, inf and finite values."""
+    rng = np.random.default_rng(123)
+    return rng.permutation(np.arange(65536, dtype=np.uint32).astype(np.uint16)).reshape(512, 128)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("gr", [1, 128])
+def test_groups_all_bit_patterns(dtype, gr):
+    check_groups(all_patterns(dtype), dtype, gr, f"all patterns {dtype} gr={gr}")
+    sorted_rows = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(512, 128)
+    check_groups(sorted_rows, dtype, gr, f"sorted patterns {dtype} gr={gr}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_groups_every_finite_amax(dtype):
+    """One 1x128 group per finite positive amax value a: x[0] = +-a and 127 random
+    patterns with magnitude key below a's, so every scale the input format can produce
+    (subnormal scales included) is exercised."""
+    top = 0x7F7F if dtype == "bf16" else 0x7BFF
+    amax_keys = np.arange(1, top + 1, dtype=np.uint32)
+    rng = np.random.default_rng(5)
+    rows = len(amax_keys)
+    body = (rng.random((rows, 127)) * amax_keys[:, None]).astype(np.uint32)      # keys below a
+    sign = (rng.integers(0, 2, (rows, 128)) << 15).astype(np.uint32)
+    bits = np.concatenate([amax_keys[:, None], body], axis=1) | sign
+    perm = rng.permuted(np.tile(np.arange(128), (rows, 1)), axis=1)
+    bits = np.take_along_axis(bits, perm, axis=1).astype(np.uint16)
+    check_groups(bits, dtype, 1, f"every amax {dtype}")
+
+
+@pytest.mark.parametrize("shape,gr", [((3, 200), 1), ((5, 136), 1), ((1, 7), 1), ((129, 129), 1),
+                                      ((17, 1000), 1), ((130, 260), 128), ((129, 129), 128),
+                                      ((300, 8), 128), ((1, 1), 128), ((257, 384), 128)])
+def test_groups_ragged(shape, gr):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    x = rng.standard_t(3, shape) * np.exp2(rng.integers(-8, 8, (shape[0], 1)))
+    check_groups(wl.to_bf16_bits(x), "bf16", gr, f"ragged {shape} gr={gr}")
+
+
+def test_weight_blocks_llama3_full():
+    _, w_bits = wl.make_inputs("llama3_8b_mlp_blockwise")
+    check_groups(w_bits, "bf16", 128, "llama3 W 128x128")
+
+
+def test_weight_blocks_deepseek_banded():
+    """W[18432, 7168]: the GPU quantizes all of it; the oracle checks block rows 0-1 and
+    the last block row (blocks are independent)."""
+    _, w_bits = wl.make_inputs("deepseek_v3_blockwise")
+    R, C = w_bits.shape
+    x = to_dev(w_bits)
+    q, s = fp8.fp8_quantize_per_token_group(x, 128, 128)
+    qh, sh = host_u8(q), host_f32(s)
+    for r0, r1 in ((0, 256), (R - 128, R)):
+        q_want, s_want = oracle.quantize_groups(w_bits[r0:r1], "bf16", 128, 128)
+        assert_bytes_equal(sh[r0 // 128:r1 // 128], s_want, f"deepseek W scales rows {r0}:{r1}")
+        assert_bytes_equal(qh[r0:r1], q_want, f"deepseek W codes rows {r0}:{r1}")
+
+
+def test_groups_deterministic():
+    a_bits, _ = wl.make_inputs("deepseek_v3_blockwise", m=128)
+    x = to_dev(a_bits)
+    q1, s1 = fp8.fp8_quantize_per_token_group(x)
+    q2, s2 = fp8.fp8_quantize_per_token_group(x)
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------- per tensor
+
+def check_tensor(bits, dtype, label):
+    R, C = bits.shape
+    q_want, s_want = oracle.quantize_per_tensor(bits, dtype)
+    x = to_dev(bits, dtype)
+    q, qfull = guarded_u8((R, C))
+    s, sfull = guarded_f32((1,))
+    fp8.fp8_quantize_per_tensor(x, q=q, scale=s)
+    assert_bytes_equal(host_f32(s), np.array([s_want], np.float32), f"{label} scale")
+    assert_bytes_equal(host_u8(q), q_want, f"{label} codes")
+    assert guard_intact(qfull, R * C, "u8") and guard_intact(sfull, 1, "f32"), label
+    a = fp8.fp8_amax(x)
+    assert_bytes_equal(host_f32(a), np.array([oracle.amax_per_tensor(oracle.input_to_f32(bits, dtype))],
+                                             np.float32), f"{label} amax")
+
+
+@pytest.mark.parametrize("which", ["a", "b"])
+def test_per_tensor_tinyllama(which):
+    a_bits, b_bits = wl.make_inputs("tinyllama_upproj_prefill")
+    check_tensor(a_bits if which == "a" else b_bits, "bf16", f"tinyllama {which}")
+
+
+def test_per_tensor_llama7b_weight():
+    _, w_bits = wl.make_inputs("llama7b_decode")
+    check_tensor(w_bits, "bf16", "llama7b W")
+
+
+def test_per_tensor_small_and_specials():
+    a_bits, b_bits = wl.make_inputs("pertensor_16x64x128")
+    check_tensor(a_bits, "bf16", "16x128")
+    check_tensor(b_bits, "bf16", "64x128")
+    for dtype in ("bf16", "f16"):
+        check_tensor(all_patterns(dtype), dtype, f"all patterns {dtype}")             # NaN amax
+        pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        key = pats & 0x7FFF
+        finite = pats[key < (0x7F80 if dtype == "bf16" else 0x7C00)]
+        check_tensor(finite[: (len(finite) // 64) * 64].reshape(-1, 64), dtype, f"finite {dtype}")
+        noinf = pats[key <= (0x7F80 if dtype == "bf16" else 0x7C00)]
+        n = (len(noinf) // 127) * 127
+        check_tensor(noinf[:n].reshape(-1, 127), dtype, f"with inf {dtype}")   # odd row length
+    check_tensor(np.zeros((33, 65), np.uint16), "bf16", "zeros")          # scale 1
+    check_tensor(np.full((7, 3), 0x8000, np.uint16), "bf16", "negative zeros")
+    check_tensor(np.array([[0x0001, 0x8001, 0x0000]], np.uint16), "bf16", "smallest subnormal amax")
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (1, 9), (1000, 1001), (2049, 3)])
+def test_per_tensor_ragged(shape):
+    rng = np.random.default_rng(shape[0] + shape[1])
+    check_tensor(wl.to_bf16_bits(rng.standard_normal(shape) * 3), "bf16", f"ragged {shape}")
+
+
+def test_per_tensor_empty():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    q, s = fp8.fp8_quantize_per_tensor(x)
+    assert q.shape == (0, 128) and float(host_f32(s)[0]) == 1.0
+    assert float(host_f32(fp8.fp8_amax(x))[0]) == 0.0
+    q, s = fp8.fp8_quantize_per_token_group(x)
+    assert q.shape == (0, 128) and s.shape == (0, 1)

@@ -172,3 +172,15 @@ def test_oracle_vs_pages_mechanism_in_torch(name):
     bnd = oracle.bound_tensorwise(qa, sa, qb, sb)
     r = oracle.check_gemm(tc.double().numpy(), c64, bnd, w.out_dtype)
     assert r["ok"], r
+
+
+def test_blockwise_row_subset_with_nblock():
+    rng = np.random.default_rng(6)
+    qa, qb = rand_codes(rng, (3, 256)), rand_codes(rng, (300, 256))
+    sa = (rng.random((3, 2)) + 0.5).astype(np.float32)
+    sb = (rng.random((3, 2)) + 0.5).astype(np.float32)
+    full = oracle.gemm_blockwise_ref(qa, sa, qb, sb)
+    cols = np.array([0, 127, 128, 200, 299])
+    sub = oracle.gemm_blockwise_ref(qa, sa, qb[cols], sb, nblock=cols // 128)
+    assert np.array_equal(sub, full[:, cols])
+

@@ -253,3 +253,12 @@ def test_quantize_with_scale_saturates():
     x = np.array([1.0, 500.0, -1000.0, 0.001], np.float32)
     q = oracle.quantize_with_scale(x, np.float32(1.0))
     assert list(q) == [0x38, 0x7E, 0xFE, oracle.encode_e4m3(np.float32(0.001))]
+
+
+def test_nan_results_are_canonical():
+    x = np.array([[1.0, np.float32(np.nan), 2.0]], np.float32)
+    x[0, 1] = np.array([0x7FC12345], np.uint32).view(np.float32)[0]      # NaN with a payload
+    assert oracle.amax_per_tensor(x).view(np.uint32) == 0x7FC00000
+    assert oracle.amax_groups(x, 1, 128).view(np.uint32)[0, 0] == 0x7FC00000
+    assert oracle.scale_from_amax(np.float32(np.nan)).view(np.uint32) == 0x7FC00000
+
