@@ -45,7 +45,7 @@ def bound_tensorwise(qa, sa, qb, sb):
     return (da @ db.T) * s
 
 
-def _slab_loop(qa, sa, qb, sb, absval):
+def _slab_loop(qa, sa, qb, sb, absval, nblock):
     qa = np.asarray(qa, dtype=np.uint8)
     qb = np.asarray(qb, dtype=np.uint8)
     M, K = qa.shape
@@ -53,7 +53,7 @@ def _slab_loop(qa, sa, qb, sb, absval):
     assert K % SLAB == 0, "blockwise operands need K to be a multiple of 128"
     sa = np.asarray(sa, dtype=np.float32).astype(np.float64)
     sb = np.asarray(sb, dtype=np.float32).astype(np.float64)
-    nblk = np.arange(N) // SLAB
+    nblk = np.arange(N) // SLAB if nblock is None else np.asarray(nblock)
     out = np.zeros((M, N), dtype=np.float64)
     for g in range(K // SLAB):
         da = _dec(qa[:, g * SLAB:(g + 1) * SLAB])
@@ -68,18 +68,20 @@ def _slab_loop(qa, sa, qb, sb, absval):
     return out
 
 
-def gemm_blockwise_ref(qa, sa, qb, sb):
+def gemm_blockwise_ref(qa, sa, qb, sb, nblock=None):
     """C64[m, n] = sum_g (sum_{k in slab g} dec(qa)dec(qb)) * sa[m, g] * sb[n // 128, g].
 
     sa is float32 [M, K/128] (one scale per token per 128 input channels), sb is
-    float32 [ceil(N/128), K/128] (one scale per 128x128 weight block).
+    float32 [ceil(N/128), K/128] (one scale per 128x128 weight block).  ``nblock``
+    optionally gives the weight-block row of each row of qb (default n // 128), so a
+    subset of B's rows can be checked against the full sb.
     """
-    return _slab_loop(qa, sa, qb, sb, absval=False)
+    return _slab_loop(qa, sa, qb, sb, False, nblock)
 
 
-def bound_blockwise(qa, sa, qb, sb):
+def bound_blockwise(qa, sa, qb, sb, nblock=None):
     """Magnitude term for the blockwise product: same sum with |.| everywhere."""
-    return _slab_loop(qa, sa, qb, sb, absval=True)
+    return _slab_loop(qa, sa, qb, sb, True, nblock)
 
 
 def output_ulp(c, out_dtype):

@@ -14,7 +14,8 @@ Readings where the pages are silent:
   usually in float32); amax / 448 and x / scale are single IEEE float32
   divisions, round to nearest even, with subnormals kept;
 * an all-zero tensor, group or block (amax = 0) gets scale 1.0 instead of 0;
-* amax propagates NaN; an infinite amax gives an infinite scale;
+* amax propagates NaN; a NaN amax or scale is the canonical quiet NaN 0x7FC00000 (so
+  results are comparable bit for bit); an infinite amax gives an infinite scale;
 * groups and blocks at a ragged edge cover only the elements that exist.
 """
 
@@ -38,7 +39,8 @@ def amax_per_tensor(x32):
     x32 = np.asarray(x32, dtype=np.float32)
     if x32.size == 0:
         return np.float32(0.0)
-    return np.float32(np.max(np.abs(x32)))
+    m = np.float32(np.max(np.abs(x32)))
+    return np.float32(np.nan) if np.isnan(m) else m
 
 
 def amax_groups(x32, group_rows, group_cols):
@@ -57,13 +59,15 @@ def amax_groups(x32, group_rows, group_cols):
     pad = np.zeros((gr * group_rows, gc * group_cols), dtype=np.float32)
     pad[:R, :C] = np.abs(x32)
     blocks = pad.reshape(gr, group_rows, gc, group_cols)
-    return blocks.max(axis=(1, 3)).astype(np.float32)
+    m = blocks.max(axis=(1, 3)).astype(np.float32)
+    return np.where(np.isnan(m), np.float32(np.nan), m).astype(np.float32)
 
 
 def scale_from_amax(amax):
     """scale = amax / 448 in float32 (Transformer Engine page §3 step 3); amax 0 -> 1.0."""
     a = np.asarray(amax, dtype=np.float32)
     s = a / np.float32(E4M3_MAX)
+    s = np.where(np.isnan(s), np.float32(np.nan), s)
     return np.where(a == 0, np.float32(1.0), s).astype(np.float32)
 
 
