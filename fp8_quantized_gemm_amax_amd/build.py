@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp8amax.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemv.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # no packed fp32 (v_pk_*_f32) instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the blockwise epilogue reads every slab's partial sums with
+    # VALU FMAs, which cannot take AGPR operands
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -222,6 +222,189 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Large-tile kernel: slabs move global -> LDS by buffer_load ... lds (LDS DMA), so no VGPRs
+// stage them and no masked branches guard them: the buffer range check returns zeros for
+// rows past M or N; K must be a multiple of 128.
+// Two stages live in distinct __shared__ arrays and the loop is unrolled by two, so the
+// compiler can tell the stage being read from the one being filled and keeps the next
+// slab's DMA in flight across the current slab's MFMAs (one barrier per slab).
+//
+// DMA layout: each wave instruction writes 64 consecutive 16-byte chunks (8 slab rows);
+// lane i of the instruction fetches logical chunk (i % 8) ^ (i / 8) of its row, which puts
+// chunk c of row r at position c ^ (r & 7) - the same swizzle the fragment reads use.
+//
+// Tile order: workgroup b runs on XCD b % 8; consecutive tiles of a grouped order
+// (groups of kGroupM tile rows) are given to the same XCD so its L2 serves their shared
+// A rows and B columns.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+#define FP8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = b % kXcds, i = b / kXcds;
+  const int logical = x * q + min(x, r) + i;
+  const int per_group = kGroupM * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_g = logical - g * per_group;
+  tm = first_m + in_g % gsize;
+  tn = in_g / gsize;
+}
+
+template <int BM, int BN, int WM, int WN, bool BLOCKWISE, int OUT>
+__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m,
+    int tiles_n) {
+  constexpr int WAVES_N = BN / WN;
+  constexpr int WAVES_M = BM / WM;
+  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(!BLOCKWISE || (WN <= 128 && 128 % WN == 0), "a wave's columns share one weight block");
+  constexpr int TM = WM / 16;
+  constexpr int TN = WN / 16;
+  constexpr int IA = BM / 32;        // DMA instructions per wave per slab
+  constexpr int IB = BN / 32;
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "whole DMA instructions");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t A0[BM * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t B0[BN * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t A1[BM * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t B1[BN * kSlab];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform (SGPR)
+  const int wm = w / WAVES_N, wn = w % WAVES_N;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int KG = K / kSlab;
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qa + static_cast<int64_t>(m0) * K), static_cast<short>(0),
+      min(BM, M - m0) * K, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qb + static_cast<int64_t>(n0) * K), static_cast<short>(0),
+      min(BN, N - n0) * K, static_cast<int>(kRsrcWord3));
+  const int lc = (lane & 7) ^ (lane >> 3);          // logical chunk this lane fetches
+  const uint32_t row_off = static_cast<uint32_t>(((w * IA) * 8 + (lane >> 3)) * K + lc * 16);
+  const uint32_t row_off_b = static_cast<uint32_t>(((w * IB) * 8 + (lane >> 3)) * K + lc * 16);
+
+  // K % 128 == 0 here (the dispatcher sends other K to the staged kernel), so every
+  // offset is plain arithmetic and only the row range check can zero a chunk
+  auto issue = [&](int s, uint8_t* As, uint8_t* Bs) {
+    const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
+#pragma unroll
+    for (int j = 0; j < IA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, FP8_LDS(As + (w * IA + j) * 1024), 16,
+                                               row_off + static_cast<uint32_t>(j * 8 * K) + k0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < IB; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, FP8_LDS(Bs + (w * IB + j) * 1024), 16,
+                                               row_off_b + static_cast<uint32_t>(j * 8 * K) + k0, 0, 0, 0);
+  };
+  auto frag = [&](const uint8_t* base, int row) -> v8i {
+    const int sw = row & 7;
+    const v4i lo = *reinterpret_cast<const v4i*>(base + row * kSlab + (((2 * kq) ^ sw) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(base + row * kSlab + (((2 * kq + 1) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  const int wave_n0 = n0 + wn * WN;
+  const int nb = wave_n0 / kSlab;
+  const int NB = (N + kSlab - 1) / kSlab;
+  auto load_scales = [&](int g, float* out) {
+    const float sbv = (nb < NB) ? sb[static_cast<int64_t>(nb) * KG + g] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm * WM + 16 * i + r16;
+      out[i] = (m < M) ? sa[static_cast<int64_t>(m) * KG + g] * sbv : 0.0f;
+    }
+  };
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  float scl[TM];
+
+  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
+    v8i af[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = frag(As, wm * WM + 16 * i + r16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const v8i bf = frag(Bs, wn * WN + 16 * j + r16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (BLOCKWISE) {
+          const v4f p = mfma_fp8(bf, af[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], scl[i], acc[i][j][r]);
+        } else {
+          acc[i][j] = mfma_fp8(bf, af[i], acc[i][j]);
+        }
+      }
+    }
+  };
+
+  // step s: wait for slab s (issued one step earlier), barrier, start slab s + 1 into the
+  // other stage, multiply slab s
+  const int nslabs = (K + kSlab - 1) / kSlab;
+  issue(0, A0, B0);
+  for (int s = 0; s < nslabs; ++s) {
+    if constexpr (BLOCKWISE) load_scales(s, scl);
+    __syncthreads();
+    const bool odd = s & 1;
+    if (s + 1 < nslabs) {
+      if (odd) issue(s + 1, A0, B0);
+      else issue(s + 1, A1, B1);
+    }
+    compute(odd ? A1 : A0, odd ? B1 : B0);
+  }
+
+  float alpha = 1.0f;
+  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  const bool vec_store = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WM + 16 * i + r16;
+    if (m >= M) continue;
+    uint16_t* crow = c + static_cast<int64_t>(m) * N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = wave_n0 + 16 * j + 4 * kq;
+      uint32_t h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * alpha);
+      if (vec_store && n + 3 < N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool BW, int OUT>
+void launch_dma(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+                int K, void* c, hipStream_t s) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  gemm_dma_kernel<BM, BN, WM, WN, BW, OUT><<<tiles_m * tiles_n, kThreads, 0, s>>>(
+      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m, tiles_n);
+}
+
 template <int BM, int BN, int WM, int WN, bool BW, int OUT>
 void launch_cfg(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
                 int K, void* c, hipStream_t s) {
@@ -235,11 +418,13 @@ template <bool BW, int OUT>
 void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
   const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + (BW ? 127 : 255)) / (BW ? 128 : 256));
-  if (M <= 16) {
+  if (M <= 16 && gemv_lds_bytes(M, K) <= 160 * 1024) {
+    launch_gemv(BW, OUT, qa, sa, qb, sb, M, N, K, c, s);
+  } else if (M <= 16) {
     launch_cfg<16, 256, 16, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-  } else if (big_tiles >= 512) {
-    if constexpr (BW) launch_cfg<256, 128, 128, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_cfg<256, 256, 128, 128, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+  } else if (big_tiles >= 512 && K % kSlab == 0) {
+    if constexpr (BW) launch_dma<128, 256, 64, 128, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_dma<256, 256, 128, 128, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
   } else {
     launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
   }

@@ -24,7 +24,12 @@ void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t*
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 
-// Scaled FP8 GEMM, C [M, N] of out_dt.
+// Decode GEMV path (M <= 16): LDS bytes it needs for the activations and its launcher.
+size_t gemv_lds_bytes(int M, int K);
+void launch_gemv(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
+                 const float* sb, int M, int N, int K, void* c, hipStream_t s);
+
+// Scaled FP8 GEMM, C [M, N] of out_dt (dispatches M <= 16 to the GEMV path).
 void launch_gemm(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
                  const float* sb, int M, int N, int K, void* c, hipStream_t s);
 
