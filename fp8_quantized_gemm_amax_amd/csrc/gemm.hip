@@ -24,6 +24,8 @@
 // consecutive output columns, stored as one 8-byte write.  Each lane supplies the same
 // 32-byte K quarter of its row for both operands, so the product is independent of the
 // order in which the hardware walks K inside the instruction.
+#include <type_traits>
+
 #include "fp8_device.hpp"
 #include "launch.hpp"
 
@@ -244,6 +246,34 @@ constexpr int kXcds = 8;
 typedef int v4i __attribute__((ext_vector_type(4)));
 #define FP8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Buffer resource for a raw byte range: 48-bit base, stride 0, `bytes` records (offsets at
+// or past it read as zero), gfx9 data-format word.  All inputs are wave-uniform.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = static_cast<int>(kRsrcWord3);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(FP8_LDS(p)));
+}
+
+// LDS DMA: every lane's 16 (or 4) bytes at `voff` in the buffer go to LDS at
+// m0 + lane * 16 (or 4).  Written as inline asm so the compiler does not treat the LDS as
+// written by an outstanding load and wait for every DMA in flight before each LDS read;
+// the kernel orders them itself (wait_vmcnt + barrier).  The instruction has no
+// destination registers, and its address operands are read when it issues.
+__device__ __forceinline__ void dma16(const v4i& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const v4i& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   const int q = total / kXcds, r = total % kXcds;
@@ -258,25 +288,51 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in_g / gsize;
 }
 
-template <int BM, int BN, int WM, int WN, bool BLOCKWISE, int OUT>
-__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds (that fence would wait
+// for every LDS DMA still in flight, i.e. for the slabs being prefetched).  The empty asm
+// statements keep the compiler from moving memory accesses across it; the caller waits
+// for the DMA it needs with wait_vmcnt first.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN>
+constexpr int dma_threads() { return 64 * (BM / WM) * (BN / WN); }
+
+template <int BM, int BN, int WM, int WN, bool BLOCKWISE, int OUT, int NS>
+__global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
     const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m,
     int tiles_n) {
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
-  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  constexpr int WAVES = WAVES_M * WAVES_N;
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(!BLOCKWISE || (WN <= 128 && 128 % WN == 0), "a wave's columns share one weight block");
+  static_assert(!BLOCKWISE || WM % 64 == 0, "one scale DMA instruction per 64 rows");
   constexpr int TM = WM / 16;
   constexpr int TN = WN / 16;
-  constexpr int IA = BM / 32;        // DMA instructions per wave per slab
-  constexpr int IB = BN / 32;
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "whole DMA instructions");
+  constexpr int IA = BM * 8 / (WAVES * 64);   // DMA instructions per wave per slab
+  constexpr int IB = BN * 8 / (WAVES * 64);
+  static_assert(IA * WAVES * 64 == BM * 8 && IB * WAVES * 64 == BN * 8, "whole DMA instructions");
+  constexpr int IS = BLOCKWISE ? WM / 64 : 0;
+  constexpr int PER_SLAB = IA + IB + IS;          // vector-memory ops per wave per slab
+  static_assert(NS == 2 || NS == 3, "two or three stages");
+  static_assert((NS - 2) * PER_SLAB < 64, "stages in flight fit vmcnt");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t A0[BM * kSlab];
-  __shared__ __attribute__((aligned(1024))) uint8_t B0[BN * kSlab];
-  __shared__ __attribute__((aligned(1024))) uint8_t A1[BM * kSlab];
-  __shared__ __attribute__((aligned(1024))) uint8_t B1[BN * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][BM * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bbuf[NS][BN * kSlab];
+  __shared__ __attribute__((aligned(16))) float Sbuf[NS][BLOCKWISE ? WAVES * WM : 1];
 
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -287,28 +343,37 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
   const int r16 = lane & 15, kq = lane >> 4;
   const int KG = K / kSlab;
 
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(qa + static_cast<int64_t>(m0) * K), static_cast<short>(0),
-      min(BM, M - m0) * K, static_cast<int>(kRsrcWord3));
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(qb + static_cast<int64_t>(n0) * K), static_cast<short>(0),
-      min(BN, N - n0) * K, static_cast<int>(kRsrcWord3));
+  const v4i ra = make_rsrc(qa + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(BM, M - m0) * K));
+  const v4i rb = make_rsrc(qb + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(min(BN, N - n0) * K));
   const int lc = (lane & 7) ^ (lane >> 3);          // logical chunk this lane fetches
   const uint32_t row_off = static_cast<uint32_t>(((w * IA) * 8 + (lane >> 3)) * K + lc * 16);
   const uint32_t row_off_b = static_cast<uint32_t>(((w * IB) * 8 + (lane >> 3)) * K + lc * 16);
+  (void)TN;
+  // blockwise: this wave's WM activation scales of a slab, one float per lane per instruction
+  const int srow0 = m0 + wm * WM;
+  v4i rs = {0, 0, 0, 0};
+  if constexpr (BLOCKWISE)
+    rs = make_rsrc(sa + static_cast<int64_t>(srow0) * KG,
+                   static_cast<uint32_t>(max(0, min(WM, M - srow0)) * KG * 4));
 
   // K % 128 == 0 here (the dispatcher sends other K to the staged kernel), so every
   // offset is plain arithmetic and only the row range check can zero a chunk
-  auto issue = [&](int s, uint8_t* As, uint8_t* Bs) {
+  auto issue = [&](int s, int st) {
     const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
+    uint8_t* As = Abuf[st];
+    uint8_t* Bs = Bbuf[st];
 #pragma unroll
     for (int j = 0; j < IA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, FP8_LDS(As + (w * IA + j) * 1024), 16,
-                                               row_off + static_cast<uint32_t>(j * 8 * K) + k0, 0, 0, 0);
+      dma16(ra, lds_addr(As + (w * IA + j) * 1024), row_off + static_cast<uint32_t>(j * 8 * K) + k0);
 #pragma unroll
     for (int j = 0; j < IB; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, FP8_LDS(Bs + (w * IB + j) * 1024), 16,
-                                               row_off_b + static_cast<uint32_t>(j * 8 * K) + k0, 0, 0, 0);
+      dma16(rb, lds_addr(Bs + (w * IB + j) * 1024), row_off_b + static_cast<uint32_t>(j * 8 * K) + k0);
+    if constexpr (BLOCKWISE) {
+      float* Ss = Sbuf[st];
+#pragma unroll
+      for (int j = 0; j < IS; ++j)
+        dma4(rs, lds_addr(Ss + w * WM + j * 64), static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+    }
   };
   auto frag = [&](const uint8_t* base, int row) -> v8i {
     const int sw = row & 7;
@@ -318,25 +383,24 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
   };
 
   const int wave_n0 = n0 + wn * WN;
-  const int nb = wave_n0 / kSlab;
-  const int NB = (N + kSlab - 1) / kSlab;
-  auto load_scales = [&](int g, float* out) {
-    const float sbv = (nb < NB) ? sb[static_cast<int64_t>(nb) * KG + g] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WM + 16 * i + r16;
-      out[i] = (m < M) ? sa[static_cast<int64_t>(m) * KG + g] * sbv : 0.0f;
-    }
-  };
+  const int nb = min(wave_n0, N - 1) / kSlab;
 
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  float scl[TM];
 
-  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
+  auto compute = [&](int s, int st) {
+    const uint8_t* As = Abuf[st];
+    const uint8_t* Bs = Bbuf[st];
+    float scl[TM];
+    if constexpr (BLOCKWISE) {
+      const float sbv = sb[static_cast<int64_t>(nb) * KG + s];
+      const float* Ss = Sbuf[st];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) scl[i] = Ss[w * WM + 16 * i + r16] * sbv;
+    }
     v8i af[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[i] = frag(As, wm * WM + 16 * i + r16);
@@ -356,19 +420,23 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
     }
   };
 
-  // step s: wait for slab s (issued one step earlier), barrier, start slab s + 1 into the
-  // other stage, multiply slab s
-  const int nslabs = (K + kSlab - 1) / kSlab;
-  issue(0, A0, B0);
+  // Pipeline: slabs s+1 .. s+NS-2 stay in flight while slab s is multiplied.  Step s waits
+  // until its own DMA for slab s has landed (everything issued later may still be
+  // outstanding), then a barrier makes every wave's part visible and tells every wave
+  // that slab s-1's stage is free again; that stage receives slab s+NS-1.
+  const int nslabs = K / kSlab;
+  issue(0, 0);
+  if (NS > 2 && nslabs > 1) issue(1, 1);
   for (int s = 0; s < nslabs; ++s) {
-    if constexpr (BLOCKWISE) load_scales(s, scl);
-    __syncthreads();
-    const bool odd = s & 1;
-    if (s + 1 < nslabs) {
-      if (odd) issue(s + 1, A0, B0);
-      else issue(s + 1, A1, B1);
+    if constexpr (NS == 3) {
+      if (s + 1 < nslabs) wait_vmcnt<PER_SLAB>();      // slab s + 1 may stay in flight
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
     }
-    compute(odd ? A1 : A0, odd ? B1 : B0);
+    stage_barrier();
+    if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS);
+    compute(s, s % NS);
   }
 
   float alpha = 1.0f;
@@ -396,12 +464,12 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool BW, int OUT>
+template <int BM, int BN, int WM, int WN, bool BW, int OUT, int NS = 2>
 void launch_dma(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
                 int K, void* c, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  gemm_dma_kernel<BM, BN, WM, WN, BW, OUT><<<tiles_m * tiles_n, kThreads, 0, s>>>(
+  gemm_dma_kernel<BM, BN, WM, WN, BW, OUT, NS><<<tiles_m * tiles_n, (dma_threads<BM, BN, WM, WN>()), 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m, tiles_n);
 }
 
@@ -417,17 +485,20 @@ void launch_cfg(const uint8_t* qa, const float* sa, const uint8_t* qb, const flo
 template <bool BW, int OUT>
 void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
-  const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + (BW ? 127 : 255)) / (BW ? 128 : 256));
   if (M <= 16 && gemv_lds_bytes(M, K) <= 160 * 1024) {
     launch_gemv(BW, OUT, qa, sa, qb, sb, M, N, K, c, s);
-  } else if (M <= 16) {
-    launch_cfg<16, 256, 16, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-  } else if (big_tiles >= 512 && K % kSlab == 0) {
-    if constexpr (BW) launch_dma<128, 256, 64, 128, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_dma<256, 256, 128, 128, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-  } else {
-    launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    return;
   }
+  if (K % kSlab != 0) {                 // K tail: the register-staged kernel zero-fills it
+    if (M <= 16) launch_cfg<16, 256, 16, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    return;
+  }
+  // 256x256 tiles (eight waves of 64x128) once there is at least one per CU; otherwise
+  // 128x128 tiles (four waves of 64x64, two workgroups per CU)
+  const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 256) launch_dma<256, 256, 64, 128, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
+  else launch_dma<128, 128, 64, 64, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
