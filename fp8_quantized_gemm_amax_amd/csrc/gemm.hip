@@ -26,6 +26,7 @@
 // order in which the hardware walks K inside the instruction.
 #include <type_traits>
 
+#include "dma.hpp"
 #include "fp8_device.hpp"
 #include "launch.hpp"
 
@@ -239,40 +240,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
 // Tile order: workgroup b runs on XCD b % 8; consecutive tiles of a grouped order
 // (groups of kGroupM tile rows) are given to the same XCD so its L2 serves their shared
 // A rows and B columns.
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-#define FP8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// Buffer resource for a raw byte range: 48-bit base, stride 0, `bytes` records (offsets at
-// or past it read as zero), gfx9 data-format word.  All inputs are wave-uniform.
-__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff));
-  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  r[3] = static_cast<int>(kRsrcWord3);
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(FP8_LDS(p)));
-}
-
-// LDS DMA: every lane's 16 (or 4) bytes at `voff` in the buffer go to LDS at
-// m0 + lane * 16 (or 4).  Written as inline asm so the compiler does not treat the LDS as
-// written by an outstanding load and wait for every DMA in flight before each LDS read;
-// the kernel orders them itself (wait_vmcnt + barrier).  The instruction has no
-// destination registers, and its address operands are read when it issues.
-__device__ __forceinline__ void dma16(const v4i& rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma4(const v4i& rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
 
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
@@ -286,24 +255,6 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   const int in_g = logical - g * per_group;
   tm = first_m + in_g % gsize;
   tn = in_g / gsize;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence __syncthreads() adds (that fence would wait
-// for every LDS DMA still in flight, i.e. for the slabs being prefetched).  The empty asm
-// statements keep the compiler from moving memory accesses across it; the caller waits
-// for the DMA it needs with wait_vmcnt first.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -485,11 +436,13 @@ void launch_cfg(const uint8_t* qa, const float* sa, const uint8_t* qb, const flo
 template <bool BW, int OUT>
 void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
-  if (M <= 16 && gemv_lds_bytes(M, K) <= 160 * 1024) {
+  if (gemv_fits(M, K)) {
     launch_gemv(BW, OUT, qa, sa, qb, sb, M, N, K, c, s);
     return;
   }
-  if (K % kSlab != 0) {                 // K tail: the register-staged kernel zero-fills it
+  // K tail: the register-staged kernel zero-fills it.  It also takes K so large that 256
+  // rows of K bytes overflow the 32-bit buffer offsets of the DMA kernel.
+  if (K % kSlab != 0 || static_cast<int64_t>(K) * 256 >= (int64_t{1} << 31)) {
     if (M <= 16) launch_cfg<16, 256, 16, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
     else launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
     return;

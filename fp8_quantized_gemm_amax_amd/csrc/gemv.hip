@@ -5,14 +5,17 @@
 // opening bullets), in the regime the task page times (batch 1): the weights are read once
 // and the product is bound by HBM bandwidth, so the kernel is built around streaming W.
 //
-// Design: one workgroup per 16 rows of W.  The activations (at most 16 rows) are staged
-// once in LDS.  Each of the four waves takes a quarter of the K slabs and streams its W
-// slabs straight from HBM into MFMA operand registers with 16-byte buffer loads (no LDS
-// round trip, no barriers in the loop), keeping kUnroll slabs in flight; rows past N read
-// as zero through the buffer range check.  One v_mfma_scale_f32_16x16x128_f8f6f4 per slab
-// (W as the first operand, A padded to 16 rows as the second) gives lane l the partial
-// sums of C[m = l % 16][n = n0 + 4 * (l / 16) + r].  The four K quarters are summed in LDS
-// and the epilogue scales and stores.
+// Design: a workgroup owns 16 * NB rows of W and its WAVES waves split the K slabs
+// between them.  Nothing goes through LDS on the way in: each wave streams its W slabs
+// straight from HBM into MFMA operand registers with 16-byte buffer loads, and fetches the
+// matching activation fragment (at most 16 rows, L2-resident after the first workgroup)
+// the same way.  The loads form a rolling pipeline: the registers of slab s are refilled
+// with slab s + UNROLL as soon as slab s has been multiplied, so UNROLL slabs stay in
+// flight per wave with no barrier in the loop.  Rows past M or N and bytes past K read as
+// zero through the buffer range check.  One v_mfma_scale_f32_16x16x128_f8f6f4 per slab and
+// row block (W as the first operand, A padded to 16 rows as the second) gives lane l the
+// partial sums of C[m = l % 16][n = n0 + 16 j + 4 (l / 16) + r].  The waves' K shares are
+// summed in LDS and the epilogue scales and stores.
 #include "fp8_device.hpp"
 #include "launch.hpp"
 
@@ -24,13 +27,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr int kSlab = 128;
-constexpr int kUnroll = 4;                 // W slabs in flight per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOOB = 0x80000000u;     // offset past any range: the load returns zeros
-constexpr int kMaxLds = 160 * 1024;
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -48,142 +47,321 @@ __device__ __forceinline__ uint32_t f32_to_out_bits(float f) {
   else return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
 }
 
-// A row stride in LDS: K plus 16 bytes, so the 16 rows a fragment read touches fall in
-// different banks.
-__host__ __device__ constexpr int a_stride(int K) { return K + 16; }
+__device__ __forceinline__ v8i load32(const __amdgpu_buffer_rsrc_t& r, uint32_t off_lo, uint32_t off_hi) {
+  const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(r, off_lo, 0, 0);
+  const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(r, off_hi, 0, 0);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
-template <bool BLOCKWISE, int OUT>
-__global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
+// WAVES waves split K; each holds UNROLL slabs in flight and multiplies NB row blocks of
+// 16 weight rows by one activation fragment.  Slabs go to the waves in turn (slab s to
+// wave s % WAVES), so at any moment a workgroup reads WAVES * 128 contiguous bytes of each
+// of its rows.
+template <bool BLOCKWISE, int OUT, int WAVES, int UNROLL, int NB>
+__global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
     const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* a_lds = smem;                                       // [M][K + 16]
-  float* red = reinterpret_cast<float*>(smem + M * a_stride(K));  // [kWaves][64][4]
+  static_assert(16 * NB <= kSlab && kSlab % (16 * NB) == 0, "a workgroup's rows share one weight block");
+  __shared__ v4f red[WAVES > 1 ? (WAVES - 1) * NB * 64 : 1];
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r16 = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NB;
   const int nslabs = (K + kSlab - 1) / kSlab;
   const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
+  const int count = (nslabs - w + WAVES - 1) / WAVES;         // this wave's slabs
+  const int iters = (count + UNROLL - 1) / UNROLL;
 
-  // stage A (M rows of K bytes) in LDS, 16 bytes per thread per step
-  for (int i = t; i < M * (K / 16); i += kThreads) {
-    const int m = i / (K / 16), k16 = i - m * (K / 16);
-    *reinterpret_cast<uint4*>(a_lds + m * a_stride(K) + k16 * 16) =
-        *reinterpret_cast<const uint4*>(qa + static_cast<int64_t>(m) * K + k16 * 16);
-  }
-
-  // this wave's slabs: an even share of [0, nslabs)
-  const int per = (nslabs + kWaves - 1) / kWaves;
-  const int s_begin = min(w * per, nslabs), s_end = min(s_begin + per, nslabs);
-
-  // W rows n0..n0+15 as one buffer; lane reads 32 bytes of row n0 + r16 per slab
-  const int rows = min(16, N - n0);
+  // W rows n0 .. n0 + 16 NB - 1 and the M activation rows as buffers; a lane reads the
+  // 32 bytes of quarter kq of a slab in row r16 of a block.  The dispatcher keeps
+  // 16 NB K and M K below 2^31, so every offset fits the 32-bit buffer offset.
+  const int rows = min(16 * NB, N - n0);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(qb + static_cast<int64_t>(n0) * K), static_cast<short>(0),
-      rows * K, static_cast<int>(kRsrcWord3));
-  const uint32_t lane_off = static_cast<uint32_t>(r16 * K + kq * 32);
-  // each 16-byte half is checked on its own: with K % 128 != 0 a lane's 32 bytes can
-  // straddle the end of the row
-  auto load_w = [&](int s) -> v8i {
-    const int kk = s * kSlab + kq * 32;
-    const uint32_t off = lane_off + s * kSlab;
-    const uint32_t off_lo = (r16 < rows && kk < K) ? off : kOOB;
-    const uint32_t off_hi = (r16 < rows && kk + 16 < K) ? off + 16 : kOOB;
-    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(wr, off_lo, 0, 0);
-    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(wr, off_hi, 0, 0);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  auto a_frag = [&](int s) -> v8i {
-    const int kk = s * kSlab + kq * 32;
-    v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-    if (r16 < M) {
-      const uint8_t* p = a_lds + r16 * a_stride(K) + kk;
-      if (kk < K) lo = *reinterpret_cast<const v4i*>(p);
-      if (kk + 16 < K) hi = *reinterpret_cast<const v4i*>(p + 16);
-    }
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  __syncthreads();
-
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      const_cast<uint8_t*>(qb + static_cast<int64_t>(n0) * K), static_cast<short>(0), rows * K,
+      static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qa), static_cast<short>(0), M * K, static_cast<int>(kRsrcWord3));
+  // blockwise scales: sa [M][KG] and this workgroup's row of sb [ceil(N/128)][KG]
   const int nb = n0 / kSlab;
-  for (int s0 = s_begin; s0 < s_end; s0 += kUnroll) {
-    v8i wf[kUnroll];
+  const __amdgpu_buffer_rsrc_t sar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(sa), static_cast<short>(0), BLOCKWISE ? M * KG * 4 : 0,
+      static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(nb) * KG : 0)), static_cast<short>(0),
+      BLOCKWISE ? KG * 4 : 0, static_cast<int>(kRsrcWord3));
+
+  // operands of this wave's i-th slab; past the wave's share every load reads zeros (the
+  // scales too, so such a slab adds 0 * 0 and a non-finite scale elsewhere cannot leak in)
+  v8i wf[UNROLL][NB], af[UNROLL];
+  float sav[UNROLL], sbv[UNROLL];
+  auto fetch = [&](int i, int u) {
+    const bool live = i < count;                              // wave-uniform
+    const int s = w + i * WAVES;
+    const int kk = s * kSlab + kq * 32;
+    const bool lo_in = live && kk < K, hi_in = live && kk + 16 < K;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) wf[u] = load_w(min(s0 + u, s_end - 1));
+    for (int j = 0; j < NB; ++j) {
+      const int row = 16 * j + r16;
+      const uint32_t off = static_cast<uint32_t>(row * K + kk);
+      wf[u][j] = load32(wr, (lo_in && row < rows) ? off : kOOB, (hi_in && row < rows) ? off + 16 : kOOB);
+    }
+    const uint32_t aoff = static_cast<uint32_t>(r16 * K + kk);
+    af[u] = load32(ar, (lo_in && r16 < M) ? aoff : kOOB, (hi_in && r16 < M) ? aoff + 16 : kOOB);
+    if constexpr (BLOCKWISE) {
+      const uint32_t soff = static_cast<uint32_t>((r16 * KG + s) * 4);
+      sav[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sar, (live && r16 < M) ? soff : kOOB, 0, 0));
+      sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, live ? static_cast<uint32_t>(s * 4) : kOOB, 0, 0));
+    }
+  };
+
+  // The first pass multiplies zero registers while the first UNROLL slabs load; from then
+  // on pass p multiplies slabs (p - 1) UNROLL + u and refetches into the same registers.
+  // Entering the loop with no load pending lets the compiler keep the steady-state wait
+  // (only the oldest slab's loads) instead of draining every load at the loop head.
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int s = s0 + u;
-      if (s >= s_end) break;
-      const v8i af = a_frag(s);
+  for (int u = 0; u < UNROLL; ++u) {
+    af[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wf[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    sav[u] = 0.0f;
+    sbv[u] = 0.0f;
+  }
+  v4f acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int it = 0; it <= iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int i = (it - 1) * UNROLL + u;
       if constexpr (BLOCKWISE) {
-        const float scale = (r16 < M) ? sa[static_cast<int64_t>(r16) * KG + s] * sb[static_cast<int64_t>(nb) * KG + s] : 0.0f;
-        const v4f p = mfma_fp8(wf[u], af, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        const float scale = sav[u] * sbv[u];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], scale, acc[r]);
+        for (int j = 0; j < NB; ++j) {
+          const v4f p = mfma_fp8(wf[u][j], af[u], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], scale, acc[j][r]);
+        }
       } else {
-        acc = mfma_fp8(wf[u], af, acc);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[j] = mfma_fp8(wf[u][j], af[u], acc[j]);
       }
+      fetch(i + UNROLL, u);
+      __builtin_amdgcn_sched_barrier(0);   // refill slot u before the next slot's math
     }
   }
 
-  // sum the four K quarters in LDS
-  *reinterpret_cast<v4f*>(red + (w * 64 + lane) * 4) = acc;
-  __syncthreads();
-  if (w != 0) return;
+  // sum the waves' K shares in LDS (wave 0 adds waves 1 .. WAVES-1 in order)
+  if constexpr (WAVES > 1) {
+    if (w > 0) {
 #pragma unroll
-  for (int q = 1; q < kWaves; ++q) {
-    const v4f o = *reinterpret_cast<const v4f*>(red + (q * 64 + lane) * 4);
+      for (int j = 0; j < NB; ++j) red[((w - 1) * NB + j) * 64 + lane] = acc[j];
+    }
+    __syncthreads();
+    if (w != 0) return;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += o[r];
+    for (int q = 1; q < WAVES; ++q)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const v4f o = red[((q - 1) * NB + j) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] += o[r];
+      }
   }
   float alpha = 1.0f;
   if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
   const int m = r16;
   if (m >= M) return;
-  const int n = n0 + 4 * kq;
-  uint32_t h[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[r] * alpha);
   uint16_t* crow = c + static_cast<int64_t>(m) * N;
-  if ((N & 3) == 0 && n + 3 < N) {
-    *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+  for (int j = 0; j < NB; ++j) {
+    const int n = n0 + 16 * j + 4 * kq;
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][r] * alpha);
+    if ((N & 3) == 0 && n + 3 < N) {
+      *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+    }
   }
 }
 
-template <bool BW, int OUT>
+// Few-token kernel (M <= MT <= 4) on the vector ALUs.  A wave owns RPW whole weight rows
+// and walks K in 1 KB chunks: each 16-byte load of a lane is bytes [1024 c + 16 l, +16) of
+// one row, so every load instruction streams 1 KB of contiguous HBM (the access pattern that
+// keeps HBM busiest) and no LDS is involved.  The 16 codes are widened exactly to f16
+// (every e4m3 value is an f16 normal) and multiplied with v_dot2c_f32_f16, which forms the
+// products exactly and accumulates in float32.  A lane's 16 K positions lie in one
+// 128-wide slab, so the blockwise scale sa[m, g] * sb[n / 128, g] is applied to each
+// lane's 16-term partial.  At the end the 64 lanes' partials of each (m, row) are summed by
+// a butterfly.  The float32 sum is ordered differently from the MFMA path; both are within
+// the product tolerance of the exact sum.
+template <bool BLOCKWISE, int OUT, int MT, int RPW, int UNROLL>
+__global__ __launch_bounds__(256) void gemv_valu_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c) {
+  static_assert(MT * RPW <= 64 && 128 % RPW == 0, "one output per lane; a wave's rows share a weight block");
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = (blockIdx.x * 4 + w) * RPW;
+  if (row0 >= N) return;                                      // no barrier in this kernel
+  const int rows = min(RPW, N - row0);
+  const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
+  const int nch = (K + 1023) / 1024;
+  const int iters = (nch + UNROLL - 1) / UNROLL;
+
+  // RPW K and M K stay below 2^31 (the dispatcher checks 32 K), so offsets fit 32 bits
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qb + static_cast<int64_t>(row0) * K), static_cast<short>(0), rows * K,
+      static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qa), static_cast<short>(0), M * K, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t sar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(sa), static_cast<short>(0), BLOCKWISE ? M * KG * 4 : 0,
+      static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(row0 / kSlab) * KG : 0)),
+      static_cast<short>(0), BLOCKWISE ? KG * 4 : 0, static_cast<int>(kRsrcWord3));
+
+  // operands of chunk i in slot u; past the last chunk every load reads zeros (the scales
+  // too, so such a chunk adds 0 * 0)
+  v4i wv[UNROLL][RPW], av[UNROLL][MT];
+  float sav[UNROLL][MT], sbv[UNROLL];
+  auto fetch = [&](int i, int u) {
+    const int col = i * 1024 + lane * 16;
+    const bool in = (i < nch) & (col < K);                   // K % 16 == 0
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      wv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, (in & (r < rows)) ? static_cast<uint32_t>(r * K + col) : kOOB, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      av[u][m] = __builtin_amdgcn_raw_buffer_load_b128(ar, (in & (m < M)) ? static_cast<uint32_t>(m * K + col) : kOOB, 0, 0);
+    if constexpr (BLOCKWISE) {
+      const int g = col >> 7;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        sav[u][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            sar, (in & (m < M)) ? static_cast<uint32_t>((m * KG + g) * 4) : kOOB, 0, 0));
+      sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, in ? static_cast<uint32_t>(g * 4) : kOOB, 0, 0));
+    }
+  };
+
+  // Same rolling scheme as the MFMA kernel: pass 0 multiplies zero registers while the
+  // first UNROLL chunks load, so the loop is entered with no load pending.
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) wv[u][r] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < MT; ++m) { av[u][m] = v4i{0, 0, 0, 0}; sav[u][m] = 0.0f; }
+    sbv[u] = 0.0f;
+  }
+  float acc[MT][RPW];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[m][r] = 0.0f;
+
+  for (int it = 0; it <= iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int i = (it - 1) * UNROLL + u;
+      h2 ah[MT][8];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          ah[m][2 * d] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[u][m][d], 1.0f, false);
+          ah[m][2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[u][m][d], 1.0f, true);
+        }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        h2 wh[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wh[2 * d] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[u][r][d], 1.0f, false);
+          wh[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[u][r][d], 1.0f, true);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float d = BLOCKWISE ? 0.0f : acc[m][r];
+#pragma unroll
+          for (int p = 0; p < 8; ++p) d = __builtin_amdgcn_fdot2(wh[p], ah[m][p], d, false);
+          if constexpr (BLOCKWISE) acc[m][r] = __builtin_fmaf(d, sav[u][m] * sbv[u], acc[m][r]);
+          else acc[m][r] = d;
+        }
+      }
+      fetch(i + UNROLL, u);
+      __builtin_amdgcn_sched_barrier(0);   // refill slot u before the next slot's math
+    }
+  }
+
+  // butterfly sum over the 64 lanes; every lane ends with every total
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc[m][r] += __shfl_xor(acc[m][r], o, 64);
+
+  float alpha = 1.0f;
+  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  // lane m * RPW + r writes C[m, row0 + r]
+  float mine = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      if (lane == m * RPW + r) mine = acc[m][r];
+  const int m = lane / RPW, r = lane % RPW;
+  if (lane < MT * RPW && m < M && r < rows)
+    c[static_cast<int64_t>(m) * N + row0 + r] = static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * alpha));
+}
+
+template <bool BW, int OUT, int MT, int RPW, int UNROLL>
+void launch_valu_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+                   int K, void* c, hipStream_t s) {
+  const int waves = (N + RPW - 1) / RPW;
+  gemv_valu_kernel<BW, OUT, MT, RPW, UNROLL><<<(waves + 3) / 4, 256, 0, s>>>(
+      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
+}
+
+template <bool BW, int OUT, int WAVES, int UNROLL, int NB>
 void launch_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
               int K, void* c, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(M) * a_stride(K) + kWaves * 64 * 4 * sizeof(float);
-  static bool attr_set = false;      // allow the full LDS of a CU for dynamic shared memory
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_fp8_kernel<BW, OUT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-    attr_set = true;
-  }
-  gemv_fp8_kernel<BW, OUT><<<(N + 15) / 16, kThreads, lds, s>>>(qa, sa, qb, sb, M, N, K,
-                                                                static_cast<uint16_t*>(c));
+  gemv_fp8_kernel<BW, OUT, WAVES, UNROLL, NB><<<(N + 16 * NB - 1) / (16 * NB), WAVES * 64, 0, s>>>(
+      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
+}
+
+// Measured on MI355X with cold weights: one token runs best on the vector-ALU kernel
+// (1 KB row streams); from two tokens on the MFMA kernel, with two row blocks per wave once
+// the activation fragment is worth sharing (M > 4).
+template <bool BW, int OUT>
+void launch_m(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+              int K, void* c, hipStream_t s) {
+  if (M == 1) launch_valu_t<BW, OUT, 1, 2, 4>(qa, sa, qb, sb, M, N, K, c, s);
+  else if (M <= 4) launch_t<BW, OUT, 2, 4, 1>(qa, sa, qb, sb, M, N, K, c, s);
+  else launch_t<BW, OUT, 4, 2, 2>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
 
-size_t gemv_lds_bytes(int M, int K) {
-  return static_cast<size_t>(M) * a_stride(K) + kWaves * 64 * 4 * sizeof(float);
+bool gemv_fits(int M, int K) {
+  return M >= 1 && M <= 16 && static_cast<int64_t>(K) * 32 < (int64_t{1} << 31);
 }
 
 void launch_gemv(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
                  const float* sb, int M, int N, int K, void* c, hipStream_t s) {
   if (blockwise) {
-    if (out_dt == DT_BF16) launch_t<true, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_t<true, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
+    if (out_dt == DT_BF16) launch_m<true, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_m<true, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
   } else {
-    if (out_dt == DT_BF16) launch_t<false, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_t<false, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
+    if (out_dt == DT_BF16) launch_m<false, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_m<false, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
   }
 }
 

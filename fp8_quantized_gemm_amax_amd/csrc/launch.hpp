@@ -24,8 +24,9 @@ void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t*
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 
-// Decode GEMV path (M <= 16): LDS bytes it needs for the activations and its launcher.
-size_t gemv_lds_bytes(int M, int K);
+// Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its
+// launcher.
+bool gemv_fits(int M, int K);
 void launch_gemv(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
                  const float* sb, int M, int N, int K, void* c, hipStream_t s);
 

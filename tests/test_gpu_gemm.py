@@ -137,11 +137,26 @@ def test_uniform_codes_within_mfma_aligned_sum_bound(mode, M, N, K):
     assert np.all(err <= tol), f"{int(np.sum(err > tol))} elements beyond the aligned-sum bound"
 
 
-def test_one_hot_layout():
+@pytest.mark.parametrize("mode", ["tensorwise", "blockwise"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("N,K", [(1, 1152), (37, 2176), (290, 640), (130, 3200)])
+def test_decode_regime_shapes(mode, M, N, K):
+    """The few-token kernels (one token on the vector ALUs, 2-4 and 5-16 tokens on the
+    MFMA GEMV): ragged N, K not a multiple of the 1 KB chunk, and for tensorwise K not a
+    multiple of 128 either."""
+    if mode == "tensorwise":
+        K += 16
+    qa, sa, qb, sb = random_case(mode, M, N, K, M * 131 + N * 7 + K)
+    got = run_gemm(mode, qa, sa, qb, sb, "bf16")
+    c64, bnd = reference(mode, qa, sa, qb, sb)
+    assert_close(got, c64, bnd, "bf16", f"{mode} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (1, 70, 1040), (5, 70, 256), (3, 33, 2064)])
+def test_one_hot_layout(M, N, K):
     """B rows one-hot at column k_n with code 1.0: C[m, n] = dec(qa[m, k_n]) * sa * sb
     exactly; a wrong lane/row mapping shows up as a wrong element."""
-    rng = np.random.default_rng(0)
-    M, N, K = 64, 64, 256
+    rng = np.random.default_rng(M + K)
     qa = rng.choice(FINITE, (M, K))
     sel = rng.integers(0, K, N)
     qb = np.zeros((N, K), np.uint8)
@@ -174,12 +189,18 @@ def test_empty_gemm_is_noop():
     assert c.shape == (4, 0)
 
 
-def test_nan_code_propagates():
+@pytest.mark.parametrize("M", [32, 1, 3])
+def test_nan_code_propagates(M):
     rng = np.random.default_rng(2)
-    qa, qb = rng.choice(FINITE, (32, 128)), rng.choice(FINITE, (32, 128))
-    qa[5, 7] = 0x7F
+    qa, qb = rng.choice(FINITE, (M, 1152)), rng.choice(FINITE, (40, 1152))
+    r = M // 2
+    qa[r, 1100] = 0x7F
     got = run_gemm("tensorwise", qa, np.float32(1.0), qb, np.float32(1.0), "bf16")
-    assert np.all(np.isnan(got[5])) and not np.any(np.isnan(np.delete(got, 5, axis=0)))
+    assert np.all(np.isnan(got[r])) and not np.any(np.isnan(np.delete(got, r, axis=0)))
+    qb[17, 3] = 0xFF
+    got = run_gemm("blockwise", qa, np.ones((M, 9), np.float32), qb, np.ones((1, 9), np.float32), "bf16")
+    assert np.all(np.isnan(got[r])) and np.all(np.isnan(got[:, 17]))
+    assert np.sum(np.isnan(got)) == got.shape[1] + got.shape[0] - 1
 
 
 # ----------------------------------------------------------------------------- workloads
