@@ -16,8 +16,10 @@
 // blockwise epilogue is one FMA per accumulator per slab.
 //
 // LDS layout: a slab tile is [rows][128 B]; the 16-byte chunk c of row r is stored at
-// chunk position c ^ (r & 7), so the 16 lanes reading one chunk column of 16 consecutive
-// rows hit distinct banks.
+// chunk position c ^ ((r >> 1) & 7).  A row is half of the 64 banks, so rows r and r + 1
+// start on opposite halves and the swizzle spreads each pair over the eight 16-byte bank
+// groups: the 16 lanes reading one chunk column of 16 consecutive rows hit 16 distinct
+// bank groups (a swizzle on r & 7 alone maps rows r and r + 8 to the same banks).
 //
 // MFMA operand roles: the first operand is the B (weight) sub-tile, the second the A
 // sub-tile, so lane l holds C[m = l % 16][n = 4 * (l / 16) + r] for r = 0..3: four
@@ -39,6 +41,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kSlab = 128;
+
+// 16-byte chunk swizzle of LDS slab rows (see the layout note above)
+__host__ __device__ constexpr int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz = blgp = 0: both operands e4m3; E8M0 scale 127 = 2^0 on both.
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       const int id = t + kThreads * j;
       if (BM * 8 % kThreads == 0 || id < BM * 8) {
         const int row = id >> 3, ch = id & 7;
-        *reinterpret_cast<uint4*>(As + row * kSlab + ((ch ^ (row & 7)) << 4)) = ra[j];
+        *reinterpret_cast<uint4*>(As + row * kSlab + ((ch ^ swz(row)) << 4)) = ra[j];
       }
     }
 #pragma unroll
@@ -127,13 +132,13 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       const int id = t + kThreads * j;
       if (BN * 8 % kThreads == 0 || id < BN * 8) {
         const int row = id >> 3, ch = id & 7;
-        *reinterpret_cast<uint4*>(Bs + row * kSlab + ((ch ^ (row & 7)) << 4)) = rb[j];
+        *reinterpret_cast<uint4*>(Bs + row * kSlab + ((ch ^ swz(row)) << 4)) = rb[j];
       }
     }
   };
   auto frag = [&](const uint8_t* base, int row) -> v8i {
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kSlab + (((2 * kq) ^ (row & 7)) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kSlab + (((2 * kq + 1) ^ (row & 7)) << 4));
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kSlab + (((2 * kq) ^ swz(row)) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kSlab + (((2 * kq + 1) ^ swz(row)) << 4));
     v8i f;
     f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
     f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
@@ -233,9 +238,11 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
 // compiler can tell the stage being read from the one being filled and keeps the next
 // slab's DMA in flight across the current slab's MFMAs (one barrier per slab).
 //
-// DMA layout: each wave instruction writes 64 consecutive 16-byte chunks (8 slab rows);
-// lane i of the instruction fetches logical chunk (i % 8) ^ (i / 8) of its row, which puts
-// chunk c of row r at position c ^ (r & 7) - the same swizzle the fragment reads use.
+// DMA layout: each wave instruction g writes 64 consecutive 16-byte chunks, rows 8g .. 8g+7;
+// lane i of the instruction fetches logical chunk (i % 8) ^ swz(8g + i / 8) of its row,
+// which puts chunk c of row r at position c ^ swz(r) - the swizzle the fragment reads use.
+// swz(8g + r') = 4 (g & 1) + r' / 2, so a lane has one source offset for even and one for
+// odd instructions.
 //
 // Tile order: workgroup b runs on XCD b % 8; consecutive tiles of a grouped order
 // (groups of kGroupM tile rows) are given to the same XCD so its L2 serves their shared
@@ -278,7 +285,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   static_assert(IA * WAVES * 64 == BM * 8 && IB * WAVES * 64 == BN * 8, "whole DMA instructions");
   constexpr int IS = BLOCKWISE ? WM / 64 : 0;
   constexpr int PER_SLAB = IA + IB + IS;          // vector-memory ops per wave per slab
-  static_assert(NS == 2 || NS == 3, "two or three stages");
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
   static_assert((NS - 2) * PER_SLAB < 64, "stages in flight fit vmcnt");
 
   __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][BM * kSlab];
@@ -296,9 +303,11 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
 
   const v4i ra = make_rsrc(qa + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(BM, M - m0) * K));
   const v4i rb = make_rsrc(qb + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(min(BN, N - n0) * K));
-  const int lc = (lane & 7) ^ (lane >> 3);          // logical chunk this lane fetches
-  const uint32_t row_off = static_cast<uint32_t>(((w * IA) * 8 + (lane >> 3)) * K + lc * 16);
-  const uint32_t row_off_b = static_cast<uint32_t>(((w * IB) * 8 + (lane >> 3)) * K + lc * 16);
+  // logical chunk this lane fetches in even and in odd DMA instructions
+  const int lc0 = (lane & 7) ^ (lane >> 4), lc1 = lc0 ^ 4;
+  const uint32_t row_off = static_cast<uint32_t>(((w * IA) * 8 + (lane >> 3)) * K);
+  const uint32_t row_off_b = static_cast<uint32_t>(((w * IB) * 8 + (lane >> 3)) * K);
+  const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
   (void)TN;
   // blockwise: this wave's WM activation scales of a slab, one float per lane per instruction
   const int srow0 = m0 + wm * WM;
@@ -315,10 +324,12 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     uint8_t* Bs = Bbuf[st];
 #pragma unroll
     for (int j = 0; j < IA; ++j)
-      dma16(ra, lds_addr(As + (w * IA + j) * 1024), row_off + static_cast<uint32_t>(j * 8 * K) + k0);
+      dma16(ra, lds_addr(As + (w * IA + j) * 1024),
+            row_off + static_cast<uint32_t>(j * 8 * K) + k0 + (((w * IA + j) & 1) ? c_odd : c_even));
 #pragma unroll
     for (int j = 0; j < IB; ++j)
-      dma16(rb, lds_addr(Bs + (w * IB + j) * 1024), row_off_b + static_cast<uint32_t>(j * 8 * K) + k0);
+      dma16(rb, lds_addr(Bs + (w * IB + j) * 1024),
+            row_off_b + static_cast<uint32_t>(j * 8 * K) + k0 + (((w * IB + j) & 1) ? c_odd : c_even));
     if constexpr (BLOCKWISE) {
       float* Ss = Sbuf[st];
 #pragma unroll
@@ -326,8 +337,9 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
         dma4(rs, lds_addr(Ss + w * WM + j * 64), static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
     }
   };
+  const int nslabs = K / kSlab;
   auto frag = [&](const uint8_t* base, int row) -> v8i {
-    const int sw = row & 7;
+    const int sw = swz(row);
     const v4i lo = *reinterpret_cast<const v4i*>(base + row * kSlab + (((2 * kq) ^ sw) << 4));
     const v4i hi = *reinterpret_cast<const v4i*>(base + row * kSlab + (((2 * kq + 1) ^ sw) << 4));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -375,16 +387,14 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   // until its own DMA for slab s has landed (everything issued later may still be
   // outstanding), then a barrier makes every wave's part visible and tells every wave
   // that slab s-1's stage is free again; that stage receives slab s+NS-1.
-  const int nslabs = K / kSlab;
-  issue(0, 0);
-  if (NS > 2 && nslabs > 1) issue(1, 1);
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nslabs) issue(p, p);
   for (int s = 0; s < nslabs; ++s) {
-    if constexpr (NS == 3) {
-      if (s + 1 < nslabs) wait_vmcnt<PER_SLAB>();      // slab s + 1 may stay in flight
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    const int ahead = min(NS - 2, nslabs - 1 - s);    // later slabs allowed to stay in flight
+    if (NS > 3 && ahead >= 2) wait_vmcnt<(NS > 3 ? 2 * PER_SLAB : 0)>();
+    else if (NS > 2 && ahead >= 1) wait_vmcnt<(NS > 2 ? PER_SLAB : 0)>();
+    else wait_vmcnt<0>();
     stage_barrier();
     if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS);
     compute(s, s % NS);
@@ -447,11 +457,17 @@ void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const 
     else launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
     return;
   }
-  // 256x256 tiles (eight waves of 64x128) once there is at least one per CU; otherwise
-  // 128x128 tiles (four waves of 64x64, two workgroups per CU)
+  // Tile choice, measured on MI355X with cold operands:
+  //  - at least one 256x256 tile per CU: 256x256, eight waves of 64x128, two stages;
+  //  - up to 128 rows (weights streamed once, few tiles): tensorwise 128x64 tiles with
+  //    four stages, blockwise 128x128 with three (more workgroups and deeper prefetch
+  //    matter more than tile reuse there);
+  //  - otherwise 128x128 tiles of eight 64x32 waves, three stages.
   const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 256) launch_dma<256, 256, 64, 128, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
-  else launch_dma<128, 128, 64, 64, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
+  else if (M <= 128 && BW) launch_dma<128, 128, 64, 64, BW, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
+  else if (M <= 128) launch_dma<128, 64, 64, 32, BW, OUT, 4>(qa, sa, qb, sb, M, N, K, c, s);
+  else launch_dma<128, 128, 64, 32, BW, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
