@@ -72,12 +72,10 @@ __device__ __forceinline__ uint8_t enc1(uint32_t h, float s, float r, bool fast)
 // ------------------------------------------------------------------------------------
 // Per-token 1x128 groups.  Sixteen lanes (one DPP row) own one group, 8 elements each.
 // Each 16-lane set takes one (row, chunk) pair: `cg` consecutive groups of one row,
-// walked kUnroll groups at a time with all loads issued before the reductions.
+// walked UNROLL groups at a time with all loads issued before the reductions.
 // Vector path: cols % 8 == 0 (a lane's eight elements are all inside or all outside).
 // WRITE_Q = false computes only the amax grid (fp8_amax with 1x128 blocks).
-constexpr int kUnroll = 2;
-
-template <int DT, bool WRITE_Q>
+template <int DT, bool WRITE_Q, int UNROLL>
 __global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t nch, int64_t cg,
     uint8_t* __restrict__ q, float* __restrict__ out) {
@@ -91,16 +89,16 @@ __global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
   const int64_t g_begin = (set - row * nch) * cg;
   const int64_t g_end = min(g_begin + cg, gcols);
   const uint16_t* xrow = x + row * cols;
-  for (int64_t g0 = g_begin; g0 < g_end; g0 += kUnroll) {
-    U4 v[kUnroll];
+  for (int64_t g0 = g_begin; g0 < g_end; g0 += UNROLL) {
+    U4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t col = ((g0 + u) << 7) + (sub << 3);
       v[u] = {0u, 0u, 0u, 0u};
       if (g0 + u < g_end && col < cols) v[u] = load16(xrow + col);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t g = g0 + u;
       if (g >= g_end) break;                       // uniform within the set
       const int64_t col = (g << 7) + (sub << 3);
@@ -312,6 +310,24 @@ constexpr int64_t kStreamCap = 256 * 16;     // 16 workgroups per CU on 256 CUs
 constexpr int64_t kReduceCap = 256 * 4;      // whole-tensor reduction workgroups
 constexpr int64_t kGroupCap = 256 * 256;     // group/block kernels loop beyond this grid
 
+// 1x128 vector path: about sets_per_cu 16-lane sets per CU, each taking cg consecutive
+// groups of one row.
+constexpr int kGroupUnroll = 2;
+constexpr int64_t kGroupSetsPerCu = 64;
+
+template <int DT, bool WRITE_Q, int UNROLL>
+void launch_group_vec(const uint16_t* xp, int64_t rows, int64_t cols, int64_t sets_per_cu, uint8_t* q,
+                      float* out, hipStream_t s) {
+  const int64_t gcols = (cols + 127) / 128;
+  const int64_t ngroups = rows * gcols;
+  const int64_t target_sets = 256 * sets_per_cu;
+  int64_t cg = (ngroups + target_sets - 1) / target_sets;
+  cg = ((cg + UNROLL - 1) / UNROLL) * UNROLL;
+  const int64_t nch = (gcols + cg - 1) / cg;
+  const unsigned grid = grid_for(rows * nch, 16, kGroupCap);
+  group_1x128_vec_kernel<DT, WRITE_Q, UNROLL><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out);
+}
+
 template <int DT>
 void launch_groups_t(const void* x, int64_t rows, int64_t cols, int32_t group_rows, uint8_t* q,
                      float* out, bool write_q, hipStream_t s) {
@@ -321,14 +337,8 @@ void launch_groups_t(const void* x, int64_t rows, int64_t cols, int32_t group_ro
     const int64_t gcols = (cols + 127) / 128;
     const int64_t ngroups = rows * gcols;
     if (vec) {
-      // aim for ~16k 16-lane sets (16 waves per CU); each takes cg consecutive groups
-      constexpr int64_t kTargetSets = 256 * 64;
-      int64_t cg = (ngroups + kTargetSets - 1) / kTargetSets;
-      cg = ((cg + kUnroll - 1) / kUnroll) * kUnroll;
-      const int64_t nch = (gcols + cg - 1) / cg;
-      const unsigned grid = grid_for(rows * nch, 16, kGroupCap);
-      if (write_q) group_1x128_vec_kernel<DT, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out);
-      else group_1x128_vec_kernel<DT, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out);
+      if (write_q) launch_group_vec<DT, true, kGroupUnroll>(xp, rows, cols, kGroupSetsPerCu, q, out, s);
+      else launch_group_vec<DT, false, kGroupUnroll>(xp, rows, cols, kGroupSetsPerCu, q, out, s);
     } else {
       const unsigned grid = grid_for(ngroups, 16, kGroupCap);
       if (write_q) group_1x128_scalar_kernel<DT, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
