@@ -130,26 +130,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   v4f acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int it = 0; it <= iters; ++it) {
+  auto consume = [&](int u) {
+    if constexpr (BLOCKWISE) {
+      const float scale = sav[u] * sbv[u];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const v4f p = mfma_fp8(wf[u][j], af[u], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], scale, acc[j][r]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] = mfma_fp8(wf[u][j], af[u], acc[j]);
+    }
+  };
+  // pass `it` multiplies slabs (it - 1) UNROLL + u of this wave and refills with
+  // it UNROLL + u; the last pass only multiplies
+  for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int i = (it - 1) * UNROLL + u;
-      if constexpr (BLOCKWISE) {
-        const float scale = sav[u] * sbv[u];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const v4f p = mfma_fp8(wf[u][j], af[u], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], scale, acc[j][r]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[j] = mfma_fp8(wf[u][j], af[u], acc[j]);
-      }
-      fetch(i + UNROLL, u);
+      consume(u);
+      fetch(it * UNROLL + u, u);
       __builtin_amdgcn_sched_barrier(0);   // refill slot u before the next slot's math
     }
   }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) consume(u);
 
   // sum the waves' K shares in LDS (wave 0 adds waves 1 .. WAVES-1 in order)
   if constexpr (WAVES > 1) {
@@ -266,39 +272,45 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
 #pragma unroll
     for (int r = 0; r < RPW; ++r) acc[m][r] = 0.0f;
 
-  for (int it = 0; it <= iters; ++it) {
+  auto consume = [&](int u) {
+    h2 ah[MT][8];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        ah[m][2 * d] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[u][m][d], 1.0f, false);
+        ah[m][2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[u][m][d], 1.0f, true);
+      }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      h2 wh[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        wh[2 * d] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[u][r][d], 1.0f, false);
+        wh[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[u][r][d], 1.0f, true);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float d = BLOCKWISE ? 0.0f : acc[m][r];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) d = __builtin_amdgcn_fdot2(wh[p], ah[m][p], d, false);
+        if constexpr (BLOCKWISE) acc[m][r] = __builtin_fmaf(d, sav[u][m] * sbv[u], acc[m][r]);
+        else acc[m][r] = d;
+      }
+    }
+  };
+  // pass `it` multiplies chunks (it - 1) UNROLL + u and refills with it UNROLL + u; the
+  // last pass only multiplies (its refills would all be past the end)
+  for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int i = (it - 1) * UNROLL + u;
-      h2 ah[MT][8];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          ah[m][2 * d] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[u][m][d], 1.0f, false);
-          ah[m][2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[u][m][d], 1.0f, true);
-        }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        h2 wh[8];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          wh[2 * d] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[u][r][d], 1.0f, false);
-          wh[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[u][r][d], 1.0f, true);
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          float d = BLOCKWISE ? 0.0f : acc[m][r];
-#pragma unroll
-          for (int p = 0; p < 8; ++p) d = __builtin_amdgcn_fdot2(wh[p], ah[m][p], d, false);
-          if constexpr (BLOCKWISE) acc[m][r] = __builtin_fmaf(d, sav[u][m] * sbv[u], acc[m][r]);
-          else acc[m][r] = d;
-        }
-      }
-      fetch(i + UNROLL, u);
+      consume(u);
+      fetch(it * UNROLL + u, u);
       __builtin_amdgcn_sched_barrier(0);   // refill slot u before the next slot's math
     }
   }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) consume(u);
 
   // butterfly sum over the 64 lanes; every lane ends with every total
 #pragma unroll
