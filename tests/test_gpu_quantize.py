@@ -182,10 +182,22 @@ def test_per_tensor_small_and_specials():
     check_tensor(np.array([[0x0001, 0x8001, 0x0000]], np.uint16), "bf16", "smallest subnormal amax")
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (1, 9), (1000, 1001), (2049, 3)])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (1, 9), (1000, 1001), (2049, 3), (1, 8191), (1, 8192),
+                                   (1, 10007), (257, 509)])
 def test_per_tensor_ragged(shape):
     rng = np.random.default_rng(shape[0] + shape[1])
     check_tensor(wl.to_bf16_bits(rng.standard_normal(shape) * 3), "bf16", f"ragged {shape}")
+
+
+@pytest.mark.parametrize("where", ["first", "last", "tail"])
+def test_per_tensor_amax_position(where):
+    """The largest element at the very start, the very end and just before the end of a
+    large tensor must each set the scale (every workgroup's share reaches the reduction)."""
+    rng = np.random.default_rng(11)
+    a = rng.standard_normal((300, 1001))
+    idx = {"first": (0, 0), "last": (299, 1000), "tail": (299, 990)}[where]
+    a[idx] = -1000.0
+    check_tensor(wl.to_bf16_bits(a), "bf16", f"amax at {where}")
 
 
 def test_per_tensor_empty():
