@@ -41,6 +41,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kSlab = 128;
+constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past any range: the load returns zeros
 
 // 16-byte chunk swizzle of LDS slab rows (see the layout note above)
 __host__ __device__ constexpr int swz(int row) { return (row >> 1) & 7; }
@@ -264,6 +265,21 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in_g / gsize;
 }
 
+// Wait until at most `ahead` slabs of PER vector-memory operations each are still in flight
+// (A = the most the pipeline ever leaves outstanding).
+template <int PER, int A>
+__device__ __forceinline__ void wait_slabs_ahead(int ahead) {
+  if constexpr (A > 0) {
+    if (ahead >= A) {
+      wait_vmcnt<A * PER>();
+      return;
+    }
+    wait_slabs_ahead<PER, A - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 template <int BM, int BN, int WM, int WN>
 constexpr int dma_threads() { return 64 * (BM / WM) * (BN / WN); }
 
@@ -285,7 +301,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   static_assert(IA * WAVES * 64 == BM * 8 && IB * WAVES * 64 == BN * 8, "whole DMA instructions");
   constexpr int IS = BLOCKWISE ? WM / 64 : 0;
   constexpr int PER_SLAB = IA + IB + IS;          // vector-memory ops per wave per slab
-  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  static_assert(NS >= 2 && NS <= 6, "two to six stages");
   static_assert((NS - 2) * PER_SLAB < 64, "stages in flight fit vmcnt");
 
   __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][BM * kSlab];
@@ -392,9 +408,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     if (p < nslabs) issue(p, p);
   for (int s = 0; s < nslabs; ++s) {
     const int ahead = min(NS - 2, nslabs - 1 - s);    // later slabs allowed to stay in flight
-    if (NS > 3 && ahead >= 2) wait_vmcnt<(NS > 3 ? 2 * PER_SLAB : 0)>();
-    else if (NS > 2 && ahead >= 1) wait_vmcnt<(NS > 2 ? PER_SLAB : 0)>();
-    else wait_vmcnt<0>();
+    wait_slabs_ahead<PER_SLAB, NS - 2>(ahead);
     stage_barrier();
     if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS);
     compute(s, s % NS);
@@ -423,6 +437,200 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
       }
     }
   }
+}
+
+// Few-token GEMM (16 < M <= 16 MB), bound by streaming W from HBM.  Every workgroup needs
+// all of A, so the cost per CU is its share of W plus one pass over A: the tile spans all
+// M rows and as few W rows as fill the chip, and no A byte is fetched twice per
+// workgroup.  The roles are split between waves so that each keeps its own in-order
+// vector-memory queue:
+//  - the last wave (the loader) stages each A slab (16 MB rows x 128 B, plus the blockwise
+//    activation scales) into an NS-deep LDS ring with LDS DMA, in the swizzled layout of
+//    the tiled kernel above;
+//  - the cw waves before it each own 16 NB weight rows and stream them from HBM straight into
+//    MFMA operand registers (UNROLL slabs in flight, refilled as soon as consumed), and
+//    multiply them by the A fragments read from LDS.
+// One barrier per slab: the loader passes it once A(s) has landed, and by reaching it the
+// compute waves have finished with slab s - 1, whose stage the loader refills next.
+// The launch has cw + 1 waves (cw <= kSkinnyMaxCw): the number of compute waves sets how
+// many weight rows a workgroup covers, and is chosen so one round of workgroups spans N.
+constexpr int kSkinnyMaxCw = 7;
+template <bool BLOCKWISE, int OUT, int NB, int MB, int NS, int UNROLL>
+__global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const float* __restrict__ sb, int M, int N, int K, int cw, uint16_t* __restrict__ c) {
+  constexpr int IA = 2 * MB;                         // A DMA instructions per slab (8 rows each)
+  constexpr int IS = BLOCKWISE ? (16 * MB + 63) / 64 : 0;   // scale DMA instructions (64 rows each)
+  constexpr int PER = IA + IS;
+  static_assert(NS >= 2 && (NS - 2) * PER < 64, "slabs in flight fit vmcnt");
+  static_assert(kSlab % (16 * NB) == 0, "a wave's rows share one weight block");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][16 * MB * kSlab];
+  __shared__ __attribute__((aligned(16))) float Sbuf[NS][BLOCKWISE ? IS * 64 : 1];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nslabs = K / kSlab;                      // K % 128 == 0 on this path
+  const int KG = nslabs;
+
+  if (w == cw) {
+    // ---- loader wave ----
+    const v4i ra = make_rsrc(qa, static_cast<uint32_t>(M * K));
+    v4i rs = {0, 0, 0, 0};
+    if constexpr (BLOCKWISE) rs = make_rsrc(sa, static_cast<uint32_t>(M * KG * 4));
+    // instruction j fetches rows 8j .. 8j + 7; lane i takes logical chunk (i % 8) ^ swz(row)
+    const int lc0 = (lane & 7) ^ (lane >> 4), lc1 = lc0 ^ 4;
+    const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
+    const uint32_t row_off = static_cast<uint32_t>((lane >> 3) * K);
+    auto issue = [&](int s, int st) {
+      const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
+#pragma unroll
+      for (int j = 0; j < IA; ++j)
+        dma16(ra, lds_addr(Abuf[st] + j * 1024),
+              row_off + static_cast<uint32_t>(j * 8 * K) + k0 + ((j & 1) ? c_odd : c_even));
+      if constexpr (BLOCKWISE) {
+#pragma unroll
+        for (int j = 0; j < IS; ++j)
+          dma4(rs, lds_addr(Sbuf[st] + j * 64), static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nslabs) issue(p, p);
+    for (int s = 0; s < nslabs; ++s) {
+      wait_slabs_ahead<PER, NS - 2>(min(NS - 2, nslabs - 1 - s));
+      stage_barrier();
+      if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS);
+    }
+    return;
+  }
+
+  // ---- compute waves ----
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int n0 = (blockIdx.x * cw + w) * 16 * NB;    // this wave's first weight row
+  // (readfirstlane keeps the clamp on the scalar unit: a VGPR range would make every
+  // buffer load a waterfall loop)
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NB, N - n0)));
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qb + static_cast<int64_t>(min(n0, N)) * K), static_cast<short>(0), rows * K,
+      static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(min(n0, N - 1) / kSlab) * KG : 0)),
+      static_cast<short>(0), BLOCKWISE && rows > 0 ? KG * 4 : 0, static_cast<int>(kRsrcWord3));
+
+  // operands of slab i in slot u; past the last slab every load reads zeros
+  v8i wf[UNROLL][NB];
+  float sbv[UNROLL];
+  auto fetch = [&](int i, int u) {
+    const bool live = i < nslabs;                    // wave-uniform
+    const uint32_t kk = static_cast<uint32_t>(i * kSlab + kq * 32);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int row = 16 * j + r16;
+      const uint32_t off = static_cast<uint32_t>(row * K) + kk;
+      const bool in = live && row < rows;
+      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? off : kOOB, 0, 0);
+      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? off + 16 : kOOB, 0, 0);
+      wf[u][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if constexpr (BLOCKWISE)
+      sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          sbr, live ? static_cast<uint32_t>(i * 4) : kOOB, 0, 0));
+  };
+  auto frag = [&](const uint8_t* base, int row) -> v8i {
+    const int sw = swz(row);
+    const v4i lo = *reinterpret_cast<const v4i*>(base + row * kSlab + (((2 * kq) ^ sw) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(base + row * kSlab + (((2 * kq + 1) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  v4f acc[NB][MB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[j][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto consume = [&](int s, int u) {
+    const int st = s % NS;
+    const uint8_t* As = Abuf[st];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const v8i af = frag(As, 16 * b + r16);
+      float scl = 0.0f;
+      if constexpr (BLOCKWISE) scl = Sbuf[st][16 * b + r16] * sbv[u];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (BLOCKWISE) {
+          const v4f p = mfma_fp8(wf[u][j], af, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][b][r] = __builtin_fmaf(p[r], scl, acc[j][b][r]);
+        } else {
+          acc[j][b] = mfma_fp8(wf[u][j], af, acc[j][b]);
+        }
+      }
+    }
+  };
+
+  // Rolling W pipeline as in the decode kernel: the first pass only loads, pass `it`
+  // multiplies slabs (it - 1) UNROLL + u and refills their registers with it UNROLL + u,
+  // and the last pass only multiplies.  Every multiplied slab is preceded by its barrier.
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wf[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    sbv[u] = 0.0f;
+  }
+  const int iters = (nslabs + UNROLL - 1) / UNROLL;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (it > 0) {
+        stage_barrier();
+        consume((it - 1) * UNROLL + u, u);
+      }
+      fetch(it * UNROLL + u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int s = (iters - 1) * UNROLL + u;
+    if (s < nslabs) {
+      stage_barrier();
+      consume(s, u);
+    }
+  }
+
+  float alpha = 1.0f;
+  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  const bool vec_store = (N & 3) == 0;
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int m = 16 * b + r16;
+    if (m >= M) continue;
+    uint16_t* crow = c + static_cast<int64_t>(m) * N;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + 16 * j + 4 * kq;
+      uint32_t h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * alpha);
+      if (vec_store && n + 3 < N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+      }
+    }
+  }
+}
+
+template <bool BW, int OUT, int NB, int MB, int NS, int UNROLL>
+void launch_skinny(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+                   int K, int cw, void* c, hipStream_t s) {
+  const int rows = 16 * cw * NB;
+  gemm_skinny_kernel<BW, OUT, NB, MB, NS, UNROLL><<<(N + rows - 1) / rows, (cw + 1) * 64, 0, s>>>(
+      qa, sa, qb, sb, M, N, K, cw, static_cast<uint16_t*>(c));
 }
 
 template <int BM, int BN, int WM, int WN, bool BW, int OUT, int NS = 2>
@@ -458,15 +666,21 @@ void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const 
     return;
   }
   // Tile choice, measured on MI355X with cold operands:
+  //  - up to 128 rows (weights streamed once): the few-token kernel, with as few compute
+  //    waves (16 weight rows each) as keep the workgroups within one round on 256 CUs,
+  //    since every workgroup also reads all of A;
   //  - at least one 256x256 tile per CU: 256x256, eight waves of 64x128, two stages;
-  //  - up to 128 rows (weights streamed once, few tiles): tensorwise 128x64 tiles with
-  //    four stages, blockwise 128x128 with three (more workgroups and deeper prefetch
-  //    matter more than tile reuse there);
   //  - otherwise 128x128 tiles of eight 64x32 waves, three stages.
+  if (M <= 128) {
+    const int cw = min(kSkinnyMaxCw, max(2, (N + 16 * 256 - 1) / (16 * 256)));
+    if (M <= 32) launch_skinny<BW, OUT, 1, 2, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    else if (M <= 64) launch_skinny<BW, OUT, 1, 4, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    else if constexpr (BW) launch_skinny<BW, OUT, 1, 8, 5, 2>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    else launch_skinny<BW, OUT, 1, 8, 5, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    return;
+  }
   const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 256) launch_dma<256, 256, 64, 128, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
-  else if (M <= 128 && BW) launch_dma<128, 128, 64, 64, BW, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
-  else if (M <= 128) launch_dma<128, 64, 64, 32, BW, OUT, 4>(qa, sa, qb, sb, M, N, K, c, s);
   else launch_dma<128, 128, 64, 32, BW, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
 }
 

@@ -54,15 +54,15 @@ __device__ __forceinline__ v8i load32(const __amdgpu_buffer_rsrc_t& r, uint32_t 
 }
 
 // WAVES waves split K; each holds UNROLL slabs in flight and multiplies NB row blocks of
-// 16 weight rows by one activation fragment.  Slabs go to the waves in turn (slab s to
-// wave s % WAVES), so at any moment a workgroup reads WAVES * 128 contiguous bytes of each
-// of its rows.
-template <bool BLOCKWISE, int OUT, int WAVES, int UNROLL, int NB>
+// 16 weight rows by MB activation fragments of 16 tokens.  Slabs go to the waves in turn
+// (slab s to wave s % WAVES), so at any moment a workgroup reads WAVES * 128 contiguous
+// bytes of each of its rows.  A workgroup's rows may straddle a 128-row weight block; the
+// blockwise scale of each row block is looked up on its own.
+template <bool BLOCKWISE, int OUT, int WAVES, int UNROLL, int NB, int MB>
 __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
     const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c) {
-  static_assert(16 * NB <= kSlab && kSlab % (16 * NB) == 0, "a workgroup's rows share one weight block");
-  __shared__ v4f red[WAVES > 1 ? (WAVES - 1) * NB * 64 : 1];
+  __shared__ v4f red[WAVES > 1 ? (WAVES - 1) * NB * MB * 64 : 1];
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -82,19 +82,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
       static_cast<int>(kRsrcWord3));
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qa), static_cast<short>(0), M * K, static_cast<int>(kRsrcWord3));
-  // blockwise scales: sa [M][KG] and this workgroup's row of sb [ceil(N/128)][KG]
-  const int nb = n0 / kSlab;
+  // blockwise scales: sa [M][KG] and the rows of sb [ceil(N/128)][KG] of the weight blocks
+  // nb0 .. nb1 this workgroup touches
+  const int nb0 = n0 / kSlab, nb1 = (n0 + rows - 1) / kSlab;
   const __amdgpu_buffer_rsrc_t sar = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(sa), static_cast<short>(0), BLOCKWISE ? M * KG * 4 : 0,
       static_cast<int>(kRsrcWord3));
   const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(nb) * KG : 0)), static_cast<short>(0),
-      BLOCKWISE ? KG * 4 : 0, static_cast<int>(kRsrcWord3));
+      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(nb0) * KG : 0)), static_cast<short>(0),
+      BLOCKWISE ? (nb1 - nb0 + 1) * KG * 4 : 0, static_cast<int>(kRsrcWord3));
 
   // operands of this wave's i-th slab; past the wave's share every load reads zeros (the
   // scales too, so such a slab adds 0 * 0 and a non-finite scale elsewhere cannot leak in)
-  v8i wf[UNROLL][NB], af[UNROLL];
-  float sav[UNROLL], sbv[UNROLL];
+  v8i wf[UNROLL][NB], af[UNROLL][MB];
+  float sav[UNROLL][MB], sbv[UNROLL][NB];
   auto fetch = [&](int i, int u) {
     const bool live = i < count;                              // wave-uniform
     const int s = w + i * WAVES;
@@ -106,12 +107,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
       const uint32_t off = static_cast<uint32_t>(row * K + kk);
       wf[u][j] = load32(wr, (lo_in && row < rows) ? off : kOOB, (hi_in && row < rows) ? off + 16 : kOOB);
     }
-    const uint32_t aoff = static_cast<uint32_t>(r16 * K + kk);
-    af[u] = load32(ar, (lo_in && r16 < M) ? aoff : kOOB, (hi_in && r16 < M) ? aoff + 16 : kOOB);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int m = 16 * b + r16;
+      const uint32_t aoff = static_cast<uint32_t>(m * K + kk);
+      af[u][b] = load32(ar, (lo_in && m < M) ? aoff : kOOB, (hi_in && m < M) ? aoff + 16 : kOOB);
+    }
     if constexpr (BLOCKWISE) {
-      const uint32_t soff = static_cast<uint32_t>((r16 * KG + s) * 4);
-      sav[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sar, (live && r16 < M) ? soff : kOOB, 0, 0));
-      sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, live ? static_cast<uint32_t>(s * 4) : kOOB, 0, 0));
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int m = 16 * b + r16;
+        const uint32_t soff = static_cast<uint32_t>((m * KG + s) * 4);
+        sav[u][b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sar, (live && m < M) ? soff : kOOB, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t soff = static_cast<uint32_t>((((n0 + 16 * j) / kSlab - nb0) * KG + s) * 4);
+        sbv[u][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, (live && 16 * j < rows) ? soff : kOOB, 0, 0));
+      }
     }
   };
 
@@ -121,28 +134,30 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   // (only the oldest slab's loads) instead of draining every load at the loop head.
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    af[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < NB; ++j) wf[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    sav[u] = 0.0f;
-    sbv[u] = 0.0f;
+    for (int b = 0; b < MB; ++b) { af[u][b] = v8i{0, 0, 0, 0, 0, 0, 0, 0}; sav[u][b] = 0.0f; }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) { wf[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0}; sbv[u][j] = 0.0f; }
   }
-  v4f acc[NB];
+  v4f acc[NB][MB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[j][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   auto consume = [&](int u) {
-    if constexpr (BLOCKWISE) {
-      const float scale = sav[u] * sbv[u];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const v4f p = mfma_fp8(wf[u][j], af[u], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], scale, acc[j][r]);
+      for (int b = 0; b < MB; ++b) {
+        if constexpr (BLOCKWISE) {
+          const float scale = sav[u][b] * sbv[u][j];
+          const v4f p = mfma_fp8(wf[u][j], af[u][b], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][b][r] = __builtin_fmaf(p[r], scale, acc[j][b][r]);
+        } else {
+          acc[j][b] = mfma_fp8(wf[u][j], af[u][b], acc[j][b]);
+        }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[j] = mfma_fp8(wf[u][j], af[u], acc[j]);
-    }
   };
   // pass `it` multiplies slabs (it - 1) UNROLL + u of this wave and refills with
   // it UNROLL + u; the last pass only multiplies
@@ -161,36 +176,43 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   if constexpr (WAVES > 1) {
     if (w > 0) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) red[((w - 1) * NB + j) * 64 + lane] = acc[j];
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) red[(((w - 1) * NB + j) * MB + b) * 64 + lane] = acc[j][b];
     }
     __syncthreads();
     if (w != 0) return;
 #pragma unroll
     for (int q = 1; q < WAVES; ++q)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const v4f o = red[((q - 1) * NB + j) * 64 + lane];
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] += o[r];
-      }
+        for (int b = 0; b < MB; ++b) {
+          const v4f o = red[(((q - 1) * NB + j) * MB + b) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][b][r] += o[r];
+        }
   }
   float alpha = 1.0f;
   if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
-  const int m = r16;
-  if (m >= M) return;
-  uint16_t* crow = c + static_cast<int64_t>(m) * N;
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int n = n0 + 16 * j + 4 * kq;
-    uint32_t h[4];
+  for (int b = 0; b < MB; ++b) {
+    const int m = 16 * b + r16;
+    if (m >= M) continue;
+    uint16_t* crow = c + static_cast<int64_t>(m) * N;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][r] * alpha);
-    if ((N & 3) == 0 && n + 3 < N) {
-      *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    } else {
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + 16 * j + 4 * kq;
+      uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * alpha);
+      if ((N & 3) == 0 && n + 3 < N) {
+        *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) crow[n + r] = static_cast<uint16_t>(h[r]);
+      }
     }
   }
 }
@@ -342,10 +364,10 @@ void launch_valu_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const 
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
 }
 
-template <bool BW, int OUT, int WAVES, int UNROLL, int NB>
+template <bool BW, int OUT, int WAVES, int UNROLL, int NB, int MB = 1>
 void launch_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
               int K, void* c, hipStream_t s) {
-  gemv_fp8_kernel<BW, OUT, WAVES, UNROLL, NB><<<(N + 16 * NB - 1) / (16 * NB), WAVES * 64, 0, s>>>(
+  gemv_fp8_kernel<BW, OUT, WAVES, UNROLL, NB, MB><<<(N + 16 * NB - 1) / (16 * NB), WAVES * 64, 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
 }
 

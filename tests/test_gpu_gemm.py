@@ -152,7 +152,23 @@ def test_decode_regime_shapes(mode, M, N, K):
     assert_close(got, c64, bnd, "bf16", f"{mode} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (1, 70, 1040), (5, 70, 256), (3, 33, 2064)])
+@pytest.mark.parametrize("mode", ["tensorwise", "blockwise"])
+@pytest.mark.parametrize("M", [17, 32, 33, 64, 65, 128])
+@pytest.mark.parametrize("N,K", [(40, 128), (290, 640), (4100, 256), (12300, 384), (29000, 128)])
+def test_few_token_regime_shapes(mode, M, N, K):
+    """The 17-128 token kernel (one loader wave, weight rows streamed into registers): a
+    single K slab (fewer than the pipeline's stages), exactly as many slabs as stages, a
+    compute wave wholly past N (N = 40), ragged last workgroups, and N from two to seven
+    compute waves per workgroup (29000 rows also needs more than one round of
+    workgroups)."""
+    qa, sa, qb, sb = random_case(mode, M, N, K, M * 17 + N * 3 + K)
+    got = run_gemm(mode, qa, sa, qb, sb, "bf16")
+    c64, bnd = reference(mode, qa, sa, qb, sb)
+    assert_close(got, c64, bnd, "bf16", f"{mode} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (1, 70, 1040), (5, 70, 256), (3, 33, 2064), (128, 300, 256),
+                                   (20, 70, 384)])
 def test_one_hot_layout(M, N, K):
     """B rows one-hot at column k_n with code 1.0: C[m, n] = dec(qa[m, k_n]) * sa * sb
     exactly; a wrong lane/row mapping shows up as a wrong element."""
