@@ -670,7 +670,9 @@ void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const 
   //    waves (16 weight rows each) as keep the workgroups within one round on 256 CUs,
   //    since every workgroup also reads all of A;
   //  - at least one 256x256 tile per CU: 256x256, eight waves of 64x128, two stages;
-  //  - otherwise 128x128 tiles of eight 64x32 waves, three stages.
+  //  - more than one 128x128 tile per CU: 128x128 tiles of four 64x64 waves with two
+  //    stages, so that two workgroups share a CU;
+  //  - otherwise (one partial round) 128x128 tiles of eight 64x32 waves, three stages.
   if (M <= 128) {
     const int cw = min(kSkinnyMaxCw, max(2, (N + 16 * 256 - 1) / (16 * 256)));
     if (M <= 32) launch_skinny<BW, OUT, 1, 2, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
@@ -680,7 +682,9 @@ void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const 
     return;
   }
   const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tiles = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
   if (big_tiles >= 256) launch_dma<256, 256, 64, 128, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
+  else if (tiles > 256) launch_dma<128, 128, 64, 64, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
   else launch_dma<128, 128, 64, 32, BW, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
 }
 

@@ -84,10 +84,13 @@ def test_blockwise_shapes(M, N, K, out_dtype):
 
 
 @pytest.mark.parametrize("mode,M,N,K", [("tensorwise", 2050, 8200, 256), ("blockwise", 2049, 8195, 384),
-                                        ("tensorwise", 4100, 4097, 128), ("blockwise", 520, 33000, 256)])
+                                        ("tensorwise", 4100, 4097, 128), ("blockwise", 520, 33000, 256),
+                                        ("tensorwise", 1030, 4100, 384), ("blockwise", 1030, 4100, 256)])
 def test_large_tile_path_ragged(mode, M, N, K):
-    """Shapes with at least one 256x256 tile per CU (the eight-wave kernel) and ragged
-    M and N edges, checked element by element over the whole output."""
+    """Shapes with at least one 256x256 tile per CU (the eight-wave kernel), or more than
+    one 128x128 tile per CU but fewer 256x256 tiles than CUs (the four-wave two-stage
+    kernel, 1030 x 4100), with ragged M and N edges, checked element by element over the
+    whole output."""
     qa, sa, qb, sb = random_case(mode, M, N, K, M + N + K)
     got = run_gemm(mode, qa, sa, qb, sb, "bf16")
     c64, bnd = reference(mode, qa, sa, qb, sb)
