@@ -92,8 +92,7 @@ fp8_status_t fp8_quantize_per_tensor(const void* x, fp8_dtype_t dt, int64_t rows
   if ((x && !aligned16(x)) || (q && !aligned16(q)) || !aligned4(scale)) return FP8_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  fp8amax::launch_tensor_reduce(static_cast<int>(dt), x, n, scale, true, s);
-  if (n > 0) fp8amax::launch_tensor_cast(static_cast<int>(dt), x, n, scale, q, s);
+  fp8amax::launch_tensor_quantize(static_cast<int>(dt), x, n, scale, q, s);
   return finish_launch();
 }
 

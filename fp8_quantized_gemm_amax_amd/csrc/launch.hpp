@@ -17,6 +17,11 @@ void launch_groups(int dt, const void* x, int64_t rows, int64_t cols, int32_t gr
 void launch_tensor_reduce(int dt, const void* x, int64_t n, float* word, bool want_scale,
                           hipStream_t s);
 
+// Whole-tensor quantize of n elements: the scale word and the codes.  Small tensors take
+// one single-workgroup launch; larger ones launch_tensor_reduce + launch_tensor_cast.
+void launch_tensor_quantize(int dt, const void* x, int64_t n, float* scale, uint8_t* q,
+                            hipStream_t s);
+
 // q[i] = e4m3(x[i] / scale) for n > 0 elements, with the scale taken from (and written
 // back to) the word launch_tensor_reduce left.
 void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t* q,

@@ -292,6 +292,53 @@ __global__ __launch_bounds__(kThreads) void tensor_cast_kernel(const uint16_t* _
   for (int64_t j = (nvec << 3) + tid; j < n; j += stride) q[j] = enc1<DT>(x[j], scale, r, fast);
 }
 
+// Whole-tensor amax, scale and cast in one workgroup, for tensors small enough that one
+// CU streams them in less time than the three-launch path spends on launches (the
+// activations of decode steps).  No atomics and no result word to clear: the workgroup
+// reduces in LDS, writes the finished float, and casts from the same scale.  The second
+// pass re-reads x, which the first pass has just brought into the caches.
+constexpr int kSmallThreads = 1024;
+
+template <int DT, bool WANT_SCALE, bool WRITE_Q>
+__global__ __launch_bounds__(kSmallThreads) void tensor_small_kernel(const uint16_t* __restrict__ x,
+                                                                     int64_t n, uint32_t* word,
+                                                                     uint8_t* __restrict__ q) {
+  __shared__ uint32_t wave_max[kSmallThreads / 64];
+  __shared__ float result;
+  const int t = threadIdx.x;
+  const int64_t nvec = n >> 3;
+  uint32_t m = 0;
+  int64_t i = t;
+  for (; i + 3 * kSmallThreads < nvec; i += 4 * kSmallThreads) {   // four loads in flight per lane
+    const U4 v0 = load16(x + (i << 3)), v1 = load16(x + ((i + kSmallThreads) << 3));
+    const U4 v2 = load16(x + ((i + 2 * kSmallThreads) << 3)), v3 = load16(x + ((i + 3 * kSmallThreads) << 3));
+    m = max(max(m, max(key8(v0), key8(v1))), max(key8(v2), key8(v3)));
+  }
+  for (; i < nvec; i += kSmallThreads) m = max(m, key8(load16(x + (i << 3))));
+  for (int64_t j = (nvec << 3) + t; j < n; j += kSmallThreads) m = max(m, x[j] & 0x7fffu);
+  m = max64(m);
+  if ((t & 63) == 0) wave_max[t >> 6] = m;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t k = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) k = max(k, wave_max[w]);
+    const float amax = amax_from_key<DT>(k);
+    const float r = WANT_SCALE ? scale_from_amax(amax) : amax;
+    result = r;
+    *word = __float_as_uint(r);
+  }
+  if constexpr (WRITE_Q) {
+    __syncthreads();
+    const float scale = result;
+    const bool fast = fast_scale(scale);
+    const float r = 1.0f / scale;
+    for (int64_t v = t; v < nvec; v += kSmallThreads)
+      *reinterpret_cast<uint2*>(q + (v << 3)) = enc8<DT>(load16(x + (v << 3)), scale, r, fast);
+    for (int64_t j = (nvec << 3) + t; j < n; j += kSmallThreads) q[j] = enc1<DT>(x[j], scale, r, fast);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void debug_cast_kernel(const float* __restrict__ v, int64_t n,
                                                               uint8_t* __restrict__ q) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -307,6 +354,7 @@ inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
 }
 
 constexpr int64_t kStreamCap = 256 * 16;     // 16 workgroups per CU on 256 CUs
+constexpr int64_t kSmallTensor = int64_t{1} << 15;   // whole-tensor path in one workgroup up to here
 constexpr int64_t kReduceCap = 256 * 4;      // whole-tensor reduction workgroups
 constexpr int64_t kGroupCap = 256 * 256;     // group/block kernels loop beyond this grid
 
@@ -359,6 +407,12 @@ void launch_groups_t(const void* x, int64_t rows, int64_t cols, int32_t group_ro
 template <int DT>
 void launch_tensor_reduce_t(const void* x, int64_t n, float* word, bool want_scale, hipStream_t s) {
   uint32_t* w = reinterpret_cast<uint32_t*>(word);
+  if (n <= kSmallTensor) {                     // one workgroup, one launch
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    if (want_scale) tensor_small_kernel<DT, true, false><<<1, kSmallThreads, 0, s>>>(xp, n, w, nullptr);
+    else tensor_small_kernel<DT, false, false><<<1, kSmallThreads, 0, s>>>(xp, n, w, nullptr);
+    return;
+  }
   init_word_kernel<<<1, 1, 0, s>>>(w);
   const unsigned grid = grid_for(n, kThreads * 8 * 4, kReduceCap);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
@@ -380,6 +434,19 @@ void launch_tensor_reduce(int dt, const void* x, int64_t n, float* word, bool wa
                           hipStream_t s) {
   if (dt == DT_BF16) launch_tensor_reduce_t<DT_BF16>(x, n, word, want_scale, s);
   else launch_tensor_reduce_t<DT_F16>(x, n, word, want_scale, s);
+}
+
+void launch_tensor_quantize(int dt, const void* x, int64_t n, float* scale, uint8_t* q,
+                            hipStream_t s) {
+  if (n > kSmallTensor) {
+    launch_tensor_reduce(dt, x, n, scale, true, s);
+    launch_tensor_cast(dt, x, n, scale, q, s);
+    return;
+  }
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint32_t* w = reinterpret_cast<uint32_t*>(scale);
+  if (dt == DT_BF16) tensor_small_kernel<DT_BF16, true, true><<<1, kSmallThreads, 0, s>>>(xp, n, w, q);
+  else tensor_small_kernel<DT_F16, true, true><<<1, kSmallThreads, 0, s>>>(xp, n, w, q);
 }
 
 void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t* q,

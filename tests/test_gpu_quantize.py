@@ -183,19 +183,24 @@ def test_per_tensor_small_and_specials():
 
 
 @pytest.mark.parametrize("shape", [(1, 1), (3, 5), (1, 9), (1000, 1001), (2049, 3), (1, 8191), (1, 8192),
-                                   (1, 10007), (257, 509)])
+                                   (1, 10007), (257, 509), (1, 4096), (1, 32768), (128, 256), (181, 181),
+                                   (1, 32776), (1, 7168)])
 def test_per_tensor_ragged(shape):
+    """Ragged sizes on both per-tensor paths: up to 32768 elements one workgroup reduces,
+    scales and casts in one launch; beyond that three launches."""
     rng = np.random.default_rng(shape[0] + shape[1])
     check_tensor(wl.to_bf16_bits(rng.standard_normal(shape) * 3), "bf16", f"ragged {shape}")
 
 
+@pytest.mark.parametrize("rows", [300, 31])
 @pytest.mark.parametrize("where", ["first", "last", "tail"])
-def test_per_tensor_amax_position(where):
+def test_per_tensor_amax_position(where, rows):
     """The largest element at the very start, the very end and just before the end of a
-    large tensor must each set the scale (every workgroup's share reaches the reduction)."""
+    tensor must each set the scale: every workgroup's share reaches the reduction (300
+    rows, three launches), and every wave's share in the one-workgroup path (31 rows)."""
     rng = np.random.default_rng(11)
-    a = rng.standard_normal((300, 1001))
-    idx = {"first": (0, 0), "last": (299, 1000), "tail": (299, 990)}[where]
+    a = rng.standard_normal((rows, 1001))
+    idx = {"first": (0, 0), "last": (rows - 1, 1000), "tail": (rows - 1, 990)}[where]
     a[idx] = -1000.0
     check_tensor(wl.to_bf16_bits(a), "bf16", f"amax at {where}")
 
