@@ -22,6 +22,11 @@ It is a plain, slow, obviously correct restatement of what the pages define:
   tolerance check.  Sources: the Transformer Engine page §3 steps 5-6 and its
   pseudocode; "FP8 chi tiết", opening bullets.
 
+* ``ue8m0`` - power-of-two block scales stored as e8m0fnu bytes: the smallest
+  power of two not below amax / 448, the cast with it, and the blockwise product
+  with the decoded scales.  Source: "FP8 chi tiết", section on the UE8M0 scale
+  format.
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
 pages print (tests/golden), closed forms, brute force over all 256 codes, exact
 rational arithmetic and library special cases.  No function is "parity
@@ -38,6 +43,8 @@ from .quant import (input_to_f32, amax_per_tensor, amax_groups, scale_from_amax,
                     quantize_per_tensor, quantize_groups, quantize_with_scale)
 from .gemm import (gemm_tensorwise_ref, gemm_blockwise_ref, bound_tensorwise,
                    bound_blockwise, output_ulp, check_gemm)
+from .ue8m0 import (e8m0_decode, e8m0_from_amax, quantize_groups_ue8m0,
+                    gemm_blockwise_ue8m0_ref, bound_blockwise_ue8m0)
 
 __all__ = [
     "E4M3_MAX", "decode_e4m3", "positive_values", "encode_e4m3", "nonneg_breakpoints",
@@ -45,4 +52,6 @@ __all__ = [
     "quantize_per_tensor", "quantize_groups", "quantize_with_scale",
     "gemm_tensorwise_ref", "gemm_blockwise_ref", "bound_tensorwise", "bound_blockwise",
     "output_ulp", "check_gemm",
+    "e8m0_decode", "e8m0_from_amax", "quantize_groups_ue8m0", "gemm_blockwise_ue8m0_ref",
+    "bound_blockwise_ue8m0",
 ]
