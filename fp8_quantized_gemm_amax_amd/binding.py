@@ -30,6 +30,8 @@ _SIGNATURES = {
     "fp8_quantize_per_token_group": ([_P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "fp8_gemm_scaled_tensorwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_gemm_scaled_blockwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "fp8_quantize_per_token_group_ue8m0": ([_P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "fp8_gemm_scaled_blockwise_ue8m0": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
 }
 
@@ -158,7 +160,31 @@ def fp8_quantize_per_token_group(x, group_rows=1, group_cols=128, q=None, scales
     return q, scales
 
 
-def _gemm(name, qa, sa, qb, sb, out_dtype, out):
+def e8m0_row_bytes(groups):
+    """Bytes per row of a UE8M0 scale tensor with `groups` scales (four per 32-bit word)."""
+    return (groups + 3) // 4 * 4
+
+
+def fp8_quantize_per_token_group_ue8m0(x, group_rows=1, group_cols=128, q=None, scales=None):
+    """Like fp8_quantize_per_token_group with power-of-two (UE8M0) scales.  Returns
+    (q uint8 [R, C], scales uint8 e8m0fnu [ceil(R/group_rows), G4]) where G4 is
+    ceil(C/group_cols) rounded up to a multiple of 4; the padding bytes are 127."""
+    x = _as_2d(x)
+    _need_cuda(x)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((-(-R // max(group_rows, 1)), e8m0_row_bytes(-(-C // max(group_cols, 1)))),
+                             dtype=torch.uint8, device=x.device)
+    _need_cuda(q, scales)
+    _check("fp8_quantize_per_token_group_ue8m0",
+           lib().fp8_quantize_per_token_group_ue8m0(_ptr(x), _dt(x), R, C, group_rows, group_cols,
+                                                    _ptr(q), _ptr(scales), _stream(x)))
+    return q, scales
+
+
+def _gemm(name, qa, sa, qb, sb, out_dtype, out, scale_dtype=torch.float32):
     qa, qb = _codes(_as_2d(qa)), _codes(_as_2d(qb))
     _need_cuda(qa, qb, sa, sb)
     M, K = qa.shape
@@ -167,8 +193,8 @@ def _gemm(name, qa, sa, qb, sb, out_dtype, out):
         raise ValueError(f"K mismatch: qa has {K}, qb has {K2}")
     sa = sa.contiguous()
     sb = sb.contiguous()
-    if sa.dtype != torch.float32 or sb.dtype != torch.float32:
-        raise TypeError("scales must be float32")
+    if sa.dtype != scale_dtype or sb.dtype != scale_dtype:
+        raise TypeError(f"scales must be {scale_dtype}")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
     _need_cuda(out)
@@ -194,6 +220,19 @@ def fp8_gemm_scaled_blockwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None
             raise ValueError(f"blockwise scales must be [{M}, {K // 128}] and [{-(-N // 128)}, {K // 128}], "
                              f"got {tuple(sa.shape)} and {tuple(sb.shape)}")
     return _gemm("fp8_gemm_scaled_blockwise", qa, sa, qb, sb, out_dtype, out)
+
+
+def fp8_gemm_scaled_blockwise_ue8m0(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
+    """Blockwise product with UE8M0 scales: sa uint8 [M, G4], sb uint8 [ceil(N/128), G4],
+    G4 = K/128 rounded up to a multiple of 4 (the layout the UE8M0 quantizer writes)."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    if K % 128 == 0 and K > 0:
+        g4 = e8m0_row_bytes(K // 128)
+        if tuple(sa.shape) != (M, g4) or tuple(sb.shape) != (-(-N // 128), g4):
+            raise ValueError(f"UE8M0 scales must be [{M}, {g4}] and [{-(-N // 128)}, {g4}], "
+                             f"got {tuple(sa.shape)} and {tuple(sb.shape)}")
+    return _gemm("fp8_gemm_scaled_blockwise_ue8m0", qa, sa, qb, sb, out_dtype, out, torch.uint8)
 
 
 def fp8_debug_cast_f32(v, q=None):

@@ -29,9 +29,10 @@ fp8_status_t finish_launch() {
   return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH;
 }
 
-fp8_status_t gemm_common(bool blockwise, const uint8_t* qa, const float* sa, const uint8_t* qb,
-                         const float* sb, int64_t M, int64_t N, int64_t K, void* c,
+fp8_status_t gemm_common(int mode, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                         const void* sb, int64_t M, int64_t N, int64_t K, void* c,
                          fp8_dtype_t out_dt, void* stream) {
+  const bool blockwise = mode != fp8amax::SM_TENSOR;
   if (M < 0 || N < 0 || K <= 0) return FP8_ERR_BAD_SHAPE;
   if (blockwise ? (K % 128 != 0) : (K % 16 != 0)) return FP8_ERR_BAD_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8_ERR_TOO_LARGE;
@@ -41,7 +42,7 @@ fp8_status_t gemm_common(bool blockwise, const uint8_t* qa, const float* sa, con
   if (!aligned16(qa) || !aligned16(qb) || !aligned16(c) || !aligned4(sa) || !aligned4(sb))
     return FP8_ERR_MISALIGNED;
   (void)hipGetLastError();   // clear a stale error so FP8_ERR_LAUNCH reports this call only
-  fp8amax::launch_gemm(blockwise, static_cast<int>(out_dt), qa, sa, qb, sb, static_cast<int>(M),
+  fp8amax::launch_gemm(mode, static_cast<int>(out_dt), qa, sa, qb, sb, static_cast<int>(M),
                        static_cast<int>(N), static_cast<int>(K), c,
                        static_cast<hipStream_t>(stream));
   return finish_launch();
@@ -115,13 +116,35 @@ fp8_status_t fp8_quantize_per_token_group(const void* x, fp8_dtype_t dt, int64_t
 fp8_status_t fp8_gemm_scaled_tensorwise(const uint8_t* qa, const float* sa, const uint8_t* qb,
                                         const float* sb, int64_t M, int64_t N, int64_t K, void* c,
                                         fp8_dtype_t out_dt, void* stream) {
-  return gemm_common(false, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
+  return gemm_common(fp8amax::SM_TENSOR, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
 }
 
 fp8_status_t fp8_gemm_scaled_blockwise(const uint8_t* qa, const float* sa, const uint8_t* qb,
                                        const float* sb, int64_t M, int64_t N, int64_t K, void* c,
                                        fp8_dtype_t out_dt, void* stream) {
-  return gemm_common(true, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
+  return gemm_common(fp8amax::SM_BLOCK, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
+}
+
+fp8_status_t fp8_quantize_per_token_group_ue8m0(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                                int32_t group_rows, int32_t group_cols, uint8_t* q,
+                                                uint8_t* scales, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  if (!group_shape_ok(group_rows, group_cols)) return FP8_ERR_BAD_SHAPE;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  if (rows * cols == 0) return FP8_OK;
+  if (!x || !q || !scales) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scales)) return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_groups_e8m0(static_cast<int>(dt), x, rows, cols, group_rows, q, scales,
+                              static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+fp8_status_t fp8_gemm_scaled_blockwise_ue8m0(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
+                                             const uint8_t* sb, int64_t M, int64_t N, int64_t K, void* c,
+                                             fp8_dtype_t out_dt, void* stream) {
+  return gemm_common(fp8amax::SM_E8M0, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
 }
 
 fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* stream) {

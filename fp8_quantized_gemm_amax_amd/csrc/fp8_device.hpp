@@ -50,6 +50,35 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
   return amax == 0.0f ? 1.0f : amax / 448.0f;
 }
 
+// UE8M0 scale code of a block (e8m0fnu byte: 2^(code - 127), 255 = NaN; fine-grained
+// FP8 page, UE8M0 scale format): the smallest power of two not below amax / 448, clamped
+// to 2^-127 .. 2^127.  amax 0 -> 2^0 (code 127); NaN or infinite amax -> 255.
+// Exact integer work on amax's bits: with amax = (1 + f) 2^E and 448 = 1.75 * 2^8,
+// 448 * 2^e >= amax holds first at e = E - 8 when 1 + f <= 1.75 (fraction bits
+// <= 0x600000) and at e = E - 7 otherwise.  A subnormal amax (< 2^-126) lies far below
+// 448 * 2^-127, so its code is the smallest one.
+__device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
+  const uint32_t b = __float_as_uint(amax) & 0x7fffffffu;
+  const uint32_t ef = b >> 23;
+  if (ef == 0xffu) return 0xffu;
+  if (ef == 0u) return b == 0u ? 127u : 0u;
+  const int e = static_cast<int>(ef) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return static_cast<uint32_t>(min(max(e, -127), 127) + 127);
+}
+
+// The float32 value of an e8m0fnu code: 2^(code - 127) exactly (code 0 is the float32
+// subnormal 2^-127), code 255 the canonical NaN.
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  if (code == 0xffu) return __uint_as_float(kCanonicalNaN);
+  return code == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23);
+}
+
+// Byte (slab & 3) of a 32-bit word holding the UE8M0 scales of four consecutive K slabs
+// (the packed layout of the UE8M0 scale tensors).
+__device__ __forceinline__ int e8m0_byte(uint32_t word, int slab) {
+  return static_cast<int>((word >> (8 * (slab & 3))) & 0xffu);
+}
+
 // Saturating round-to-nearest-even encode of a float32 to an OCP e4m3fn code.
 //   NaN -> 0x7F; |v| >= 448 (inf included) -> 0x7E with v's sign; the sign of zero and of
 //   values that round to zero is kept.

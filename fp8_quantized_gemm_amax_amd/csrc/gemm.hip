@@ -51,6 +51,13 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The same product with E8M0 block scales: each lane's 32 K positions of the first operand
+// are scaled by 2^(ea - 127) and those of the second by 2^(eb - 127) (measured on gfx950:
+// a lane's scale byte covers exactly the 32 K positions it holds, for both operands).
+__device__ __forceinline__ v4f mfma_fp8_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
@@ -66,10 +73,16 @@ __device__ __forceinline__ uint32_t f32_to_out_bits(float f) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool BLOCKWISE, int OUT>
+template <int BM, int BN, int WM, int WN, int SM, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
-    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m) {
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m) {
+  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool E8M0 = SM == SM_E8M0;
+  const float* __restrict__ sa = static_cast<const float*>(sa_);
+  const float* __restrict__ sb = static_cast<const float*>(sb_);
+  const uint8_t* __restrict__ ea_ = static_cast<const uint8_t*>(sa_);
+  const uint8_t* __restrict__ eb_ = static_cast<const uint8_t*>(sb_);
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
   static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
@@ -95,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   const int r16 = lane & 15;
   const int kq = lane >> 4;      // 32-byte quarter of the slab this lane feeds to the MFMA
   const int KG = K / kSlab;      // blockwise only (K % 128 == 0 there)
+  const int64_t KG4 = e8m0_row_bytes(KG);
 
   uint4 ra[A_IT], rb[B_IT];
   auto gload = [&](int k0) {
@@ -150,12 +164,21 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   const int wave_n0 = n0 + wn * WN;
   const int nb = wave_n0 / kSlab;
   const int NB = (N + kSlab - 1) / kSlab;
-  auto load_scales = [&](int g, float* out) {
-    const float sbv = (nb < NB) ? sb[static_cast<int64_t>(nb) * KG + g] : 0.0f;
+  auto load_scales = [&](int g, float* out, int* ea, int& eb) {
+    if constexpr (E8M0) {
+      eb = (nb < NB) ? eb_[nb * KG4 + g] : 127;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WM + 16 * i + r16;
-      out[i] = (m < M) ? sa[static_cast<int64_t>(m) * KG + g] * sbv : 0.0f;
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + 16 * i + r16;
+        ea[i] = (m < M) ? ea_[m * KG4 + g] : 127;             // rows past M multiply zeros
+      }
+    } else {
+      const float sbv = (nb < NB) ? sb[static_cast<int64_t>(nb) * KG + g] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + 16 * i + r16;
+        out[i] = (m < M) ? sa[static_cast<int64_t>(m) * KG + g] * sbv : 0.0f;
+      }
     }
   };
 
@@ -166,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   float scl[TM], scl_next[TM];
-  if constexpr (BLOCKWISE) load_scales(0, scl);
+  int ea[TM], ea_next[TM], eb = 127, eb_next = 127;
+  if constexpr (BLOCKWISE) load_scales(0, scl, ea, eb);
 
   const int nslabs = (K + kSlab - 1) / kSlab;
   gload(0);
@@ -177,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const bool more = s + 1 < nslabs;
     if (more) gload((s + 1) * kSlab);
     if constexpr (BLOCKWISE) {
-      if (more) load_scales(s + 1, scl_next);
+      if (more) load_scales(s + 1, scl_next, ea_next, eb_next);
     }
     const uint8_t* As = lds + cur * STAGE;
     const uint8_t* Bs = As + BM * kSlab;
@@ -189,7 +213,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       const v8i bf = frag(Bs, wn * WN + 16 * j + r16);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if constexpr (BLOCKWISE) {
+        if constexpr (E8M0) {
+          acc[i][j] = mfma_fp8_e8m0(bf, af[i], acc[i][j], eb, ea[i]);
+        } else if constexpr (BLOCKWISE) {
           const v4f p = mfma_fp8(bf, af[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], scl[i], acc[i][j][r]);
@@ -201,7 +227,11 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     if (more) lstore(cur ^ 1);
     if constexpr (BLOCKWISE) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) scl[i] = scl_next[i];
+      for (int i = 0; i < TM; ++i) {
+        scl[i] = scl_next[i];
+        ea[i] = ea_next[i];
+      }
+      eb = eb_next;
     }
     __syncthreads();
   }
@@ -283,11 +313,15 @@ __device__ __forceinline__ void wait_slabs_ahead(int ahead) {
 template <int BM, int BN, int WM, int WN>
 constexpr int dma_threads() { return 64 * (BM / WM) * (BN / WN); }
 
-template <int BM, int BN, int WM, int WN, bool BLOCKWISE, int OUT, int NS>
+template <int BM, int BN, int WM, int WN, int SM, int OUT, int NS>
 __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
-    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m,
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m,
     int tiles_n) {
+  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool E8M0 = SM == SM_E8M0;
+  const float* __restrict__ sa = static_cast<const float*>(sa_);
+  const float* __restrict__ sb = static_cast<const float*>(sb_);
   constexpr int WAVES_N = BN / WN;
   constexpr int WAVES_M = BM / WM;
   constexpr int WAVES = WAVES_M * WAVES_N;
@@ -316,6 +350,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   const int wm = w / WAVES_N, wn = w % WAVES_N;
   const int r16 = lane & 15, kq = lane >> 4;
   const int KG = K / kSlab;
+  const int KG4 = static_cast<int>(e8m0_row_bytes(KG));   // UE8M0: bytes per scale row
 
   const v4i ra = make_rsrc(qa + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(BM, M - m0) * K));
   const v4i rb = make_rsrc(qb + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(min(BN, N - n0) * K));
@@ -325,10 +360,14 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   const uint32_t row_off_b = static_cast<uint32_t>(((w * IB) * 8 + (lane >> 3)) * K);
   const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
   (void)TN;
-  // blockwise: this wave's WM activation scales of a slab, one float per lane per instruction
+  // blockwise: this wave's WM activation scales of a slab, one 32-bit word per lane per
+  // instruction (a float32 scale, or for UE8M0 the word holding the slab's scale byte)
   const int srow0 = m0 + wm * WM;
   v4i rs = {0, 0, 0, 0};
-  if constexpr (BLOCKWISE)
+  if constexpr (E8M0)
+    rs = make_rsrc(static_cast<const uint8_t*>(sa_) + static_cast<int64_t>(srow0) * KG4,
+                   static_cast<uint32_t>(max(0, min(WM, M - srow0)) * KG4));
+  else if constexpr (BLOCKWISE)
     rs = make_rsrc(sa + static_cast<int64_t>(srow0) * KG,
                    static_cast<uint32_t>(max(0, min(WM, M - srow0)) * KG * 4));
 
@@ -350,7 +389,9 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
       float* Ss = Sbuf[st];
 #pragma unroll
       for (int j = 0; j < IS; ++j)
-        dma4(rs, lds_addr(Ss + w * WM + j * 64), static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+        dma4(rs, lds_addr(Ss + w * WM + j * 64),
+             E8M0 ? static_cast<uint32_t>((j * 64 + lane) * KG4 + (s & ~3))
+                  : static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
     }
   };
   const int nslabs = K / kSlab;
@@ -374,7 +415,16 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     const uint8_t* As = Abuf[st];
     const uint8_t* Bs = Bbuf[st];
     float scl[TM];
-    if constexpr (BLOCKWISE) {
+    int ea[TM], eb = 127;
+    if constexpr (E8M0) {
+      // the weight block's word is wave-uniform (a scalar load); each lane's activation
+      // word came with the slab's DMA
+      eb = e8m0_byte(*reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(sb_) +
+                                                         static_cast<int64_t>(nb) * KG4 + (s & ~3)), s);
+      const float* Ss = Sbuf[st];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ea[i] = e8m0_byte(__float_as_uint(Ss[w * WM + 16 * i + r16]), s);
+    } else if constexpr (BLOCKWISE) {
       const float sbv = sb[static_cast<int64_t>(nb) * KG + s];
       const float* Ss = Sbuf[st];
 #pragma unroll
@@ -388,7 +438,9 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
       const v8i bf = frag(Bs, wn * WN + 16 * j + r16);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if constexpr (BLOCKWISE) {
+        if constexpr (E8M0) {
+          acc[i][j] = mfma_fp8_e8m0(bf, af[i], acc[i][j], eb, ea[i]);
+        } else if constexpr (BLOCKWISE) {
           const v4f p = mfma_fp8(bf, af[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], scl[i], acc[i][j][r]);
@@ -455,10 +507,14 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
 // The launch has cw + 1 waves (cw <= kSkinnyMaxCw): the number of compute waves sets how
 // many weight rows a workgroup covers, and is chosen so one round of workgroups spans N.
 constexpr int kSkinnyMaxCw = 7;
-template <bool BLOCKWISE, int OUT, int NB, int MB, int NS, int UNROLL>
+template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
 __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
-    const float* __restrict__ sb, int M, int N, int K, int cw, uint16_t* __restrict__ c) {
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb_, int M, int N, int K, int cw, uint16_t* __restrict__ c) {
+  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool E8M0 = SM == SM_E8M0;
+  const float* __restrict__ sa = static_cast<const float*>(sa_);
+  const float* __restrict__ sb = static_cast<const float*>(sb_);
   constexpr int IA = 2 * MB;                         // A DMA instructions per slab (8 rows each)
   constexpr int IS = BLOCKWISE ? (16 * MB + 63) / 64 : 0;   // scale DMA instructions (64 rows each)
   constexpr int PER = IA + IS;
@@ -472,12 +528,14 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nslabs = K / kSlab;                      // K % 128 == 0 on this path
   const int KG = nslabs;
+  const int KG4 = static_cast<int>(e8m0_row_bytes(KG));   // UE8M0: bytes per scale row
 
   if (w == cw) {
     // ---- loader wave ----
     const v4i ra = make_rsrc(qa, static_cast<uint32_t>(M * K));
     v4i rs = {0, 0, 0, 0};
-    if constexpr (BLOCKWISE) rs = make_rsrc(sa, static_cast<uint32_t>(M * KG * 4));
+    if constexpr (E8M0) rs = make_rsrc(sa_, static_cast<uint32_t>(M * KG4));
+    else if constexpr (BLOCKWISE) rs = make_rsrc(sa, static_cast<uint32_t>(M * KG * 4));
     // instruction j fetches rows 8j .. 8j + 7; lane i takes logical chunk (i % 8) ^ swz(row)
     const int lc0 = (lane & 7) ^ (lane >> 4), lc1 = lc0 ^ 4;
     const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
@@ -491,7 +549,9 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
       if constexpr (BLOCKWISE) {
 #pragma unroll
         for (int j = 0; j < IS; ++j)
-          dma4(rs, lds_addr(Sbuf[st] + j * 64), static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+          dma4(rs, lds_addr(Sbuf[st] + j * 64),
+               E8M0 ? static_cast<uint32_t>((j * 64 + lane) * KG4 + (s & ~3))
+                    : static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
       }
     };
 #pragma unroll
@@ -514,9 +574,12 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qb + static_cast<int64_t>(min(n0, N)) * K), static_cast<short>(0), rows * K,
       static_cast<int>(kRsrcWord3));
+  // this wave's weight-block row of sb: KG float32 scales, or KG4 UE8M0 bytes
+  const int64_t sb_row = static_cast<int64_t>(min(n0, N - 1) / kSlab);
   const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(min(n0, N - 1) / kSlab) * KG : 0)),
-      static_cast<short>(0), BLOCKWISE && rows > 0 ? KG * 4 : 0, static_cast<int>(kRsrcWord3));
+      E8M0 ? const_cast<uint8_t*>(static_cast<const uint8_t*>(sb_) + sb_row * KG4)
+           : static_cast<void*>(const_cast<float*>(sb + (BLOCKWISE ? sb_row * KG : 0))),
+      static_cast<short>(0), BLOCKWISE && rows > 0 ? (E8M0 ? KG4 : KG * 4) : 0, static_cast<int>(kRsrcWord3));
 
   // operands of slab i in slot u; past the last slab every load reads zeros
   v8i wf[UNROLL][NB];
@@ -533,9 +596,9 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
       const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? off + 16 : kOOB, 0, 0);
       wf[u][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    if constexpr (BLOCKWISE)
+    if constexpr (BLOCKWISE)   // UE8M0: the 32-bit word holding slab i's byte, kept as bits
       sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-          sbr, live ? static_cast<uint32_t>(i * 4) : kOOB, 0, 0));
+          sbr, live ? static_cast<uint32_t>(E8M0 ? (i & ~3) : i * 4) : kOOB, 0, 0));
   };
   auto frag = [&](const uint8_t* base, int row) -> v8i {
     const int sw = swz(row);
@@ -556,10 +619,18 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
     for (int b = 0; b < MB; ++b) {
       const v8i af = frag(As, 16 * b + r16);
       float scl = 0.0f;
-      if constexpr (BLOCKWISE) scl = Sbuf[st][16 * b + r16] * sbv[u];
+      int ea = 127, eb = 127;
+      if constexpr (E8M0) {
+        ea = e8m0_byte(__float_as_uint(Sbuf[st][16 * b + r16]), s);
+        eb = e8m0_byte(__float_as_uint(sbv[u]), s);
+      } else if constexpr (BLOCKWISE) {
+        scl = Sbuf[st][16 * b + r16] * sbv[u];
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        if constexpr (BLOCKWISE) {
+        if constexpr (E8M0) {
+          acc[j][b] = mfma_fp8_e8m0(wf[u][j], af, acc[j][b], eb, ea);
+        } else if constexpr (BLOCKWISE) {
           const v4f p = mfma_fp8(wf[u][j], af, v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[j][b][r] = __builtin_fmaf(p[r], scl, acc[j][b][r]);
@@ -625,44 +696,45 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
   }
 }
 
-template <bool BW, int OUT, int NB, int MB, int NS, int UNROLL>
-void launch_skinny(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
+void launch_skinny(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                    int K, int cw, void* c, hipStream_t s) {
   const int rows = 16 * cw * NB;
-  gemm_skinny_kernel<BW, OUT, NB, MB, NS, UNROLL><<<(N + rows - 1) / rows, (cw + 1) * 64, 0, s>>>(
+  gemm_skinny_kernel<SM, OUT, NB, MB, NS, UNROLL><<<(N + rows - 1) / rows, (cw + 1) * 64, 0, s>>>(
       qa, sa, qb, sb, M, N, K, cw, static_cast<uint16_t*>(c));
 }
 
-template <int BM, int BN, int WM, int WN, bool BW, int OUT, int NS = 2>
-void launch_dma(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int BM, int BN, int WM, int WN, int SM, int OUT, int NS = 2>
+void launch_dma(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                 int K, void* c, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  gemm_dma_kernel<BM, BN, WM, WN, BW, OUT, NS><<<tiles_m * tiles_n, (dma_threads<BM, BN, WM, WN>()), 0, s>>>(
+  gemm_dma_kernel<BM, BN, WM, WN, SM, OUT, NS><<<tiles_m * tiles_n, (dma_threads<BM, BN, WM, WN>()), 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m, tiles_n);
 }
 
-template <int BM, int BN, int WM, int WN, bool BW, int OUT>
-void launch_cfg(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int BM, int BN, int WM, int WN, int SM, int OUT>
+void launch_cfg(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                 int K, void* c, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  gemm_fp8_kernel<BM, BN, WM, WN, BW, OUT><<<tiles_m * tiles_n, kThreads, 0, s>>>(
+  gemm_fp8_kernel<BM, BN, WM, WN, SM, OUT><<<tiles_m * tiles_n, kThreads, 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m);
 }
 
-template <bool BW, int OUT>
-void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int SM, int OUT>
+void launch_gemm_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
+  constexpr bool BW = SM != SM_TENSOR;
   if (gemv_fits(M, K)) {
-    launch_gemv(BW, OUT, qa, sa, qb, sb, M, N, K, c, s);
+    launch_gemv(SM, OUT, qa, sa, qb, sb, M, N, K, c, s);
     return;
   }
   // K tail: the register-staged kernel zero-fills it.  It also takes K so large that 256
   // rows of K bytes overflow the 32-bit buffer offsets of the DMA kernel.
   if (K % kSlab != 0 || static_cast<int64_t>(K) * 256 >= (int64_t{1} << 31)) {
-    if (M <= 16) launch_cfg<16, 256, 16, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_cfg<128, 128, 64, 64, BW, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    if (M <= 16) launch_cfg<16, 256, 16, 64, SM, OUT>(qa, sa, qb, sb, M, N, K, c, s);
+    else launch_cfg<128, 128, 64, 64, SM, OUT>(qa, sa, qb, sb, M, N, K, c, s);
     return;
   }
   // Tile choice, measured on MI355X with cold operands:
@@ -675,30 +747,33 @@ void launch_gemm_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const 
   //  - otherwise (one partial round) 128x128 tiles of eight 64x32 waves, three stages.
   if (M <= 128) {
     const int cw = min(kSkinnyMaxCw, max(2, (N + 16 * 256 - 1) / (16 * 256)));
-    if (M <= 32) launch_skinny<BW, OUT, 1, 2, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    else if (M <= 64) launch_skinny<BW, OUT, 1, 4, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    else if constexpr (BW) launch_skinny<BW, OUT, 1, 8, 5, 2>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    else launch_skinny<BW, OUT, 1, 8, 5, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    if (M <= 32) launch_skinny<SM, OUT, 1, 2, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    else if (M <= 64) launch_skinny<SM, OUT, 1, 4, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    else if constexpr (BW) launch_skinny<SM, OUT, 1, 8, 5, 2>(qa, sa, qb, sb, M, N, K, cw, c, s);
+    else launch_skinny<SM, OUT, 1, 8, 5, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
     return;
   }
   const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
   const int64_t tiles = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
-  if (big_tiles >= 256) launch_dma<256, 256, 64, 128, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
-  else if (tiles > 256) launch_dma<128, 128, 64, 64, BW, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
-  else launch_dma<128, 128, 64, 32, BW, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
+  if (big_tiles >= 256) launch_dma<256, 256, 64, 128, SM, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
+  else if (tiles > 256) launch_dma<128, 128, 64, 64, SM, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
+  else launch_dma<128, 128, 64, 32, SM, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
+}
+
+template <int SM>
+void launch_gemm_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M,
+                   int N, int K, void* c, hipStream_t s) {
+  if (out_dt == DT_BF16) launch_gemm_t<SM, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
+  else launch_gemm_t<SM, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
 
-void launch_gemm(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
-                 const float* sb, int M, int N, int K, void* c, hipStream_t s) {
-  if (blockwise) {
-    if (out_dt == DT_BF16) launch_gemm_t<true, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_gemm_t<true, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
-  } else {
-    if (out_dt == DT_BF16) launch_gemm_t<false, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_gemm_t<false, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
-  }
+void launch_gemm(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                 const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (mode == SM_E8M0) launch_gemm_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  else if (mode == SM_BLOCK) launch_gemm_m<SM_BLOCK>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  else launch_gemm_m<SM_TENSOR>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace fp8amax

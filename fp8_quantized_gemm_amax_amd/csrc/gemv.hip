@@ -35,6 +35,12 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// With E8M0 block scales: a lane's 32 K positions of the first operand times 2^(ea - 127),
+// of the second times 2^(eb - 127).
+__device__ __forceinline__ v4f mfma_fp8_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
@@ -58,10 +64,14 @@ __device__ __forceinline__ v8i load32(const __amdgpu_buffer_rsrc_t& r, uint32_t 
 // (slab s to wave s % WAVES), so at any moment a workgroup reads WAVES * 128 contiguous
 // bytes of each of its rows.  A workgroup's rows may straddle a 128-row weight block; the
 // blockwise scale of each row block is looked up on its own.
-template <bool BLOCKWISE, int OUT, int WAVES, int UNROLL, int NB, int MB>
+template <int SM, int OUT, int WAVES, int UNROLL, int NB, int MB>
 __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
-    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c) {
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c) {
+  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool E8M0 = SM == SM_E8M0;
+  const float* __restrict__ sa = static_cast<const float*>(sa_);
+  const float* __restrict__ sb = static_cast<const float*>(sb_);
   __shared__ v4f red[WAVES > 1 ? (WAVES - 1) * NB * MB * 64 : 1];
 
   const int t = threadIdx.x, lane = t & 63;
@@ -70,6 +80,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   const int n0 = blockIdx.x * 16 * NB;
   const int nslabs = (K + kSlab - 1) / kSlab;
   const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
+  const int KG4 = static_cast<int>(e8m0_row_bytes(KG));      // UE8M0: bytes per scale row
+  const int SR = E8M0 ? KG4 : KG * 4;                         // bytes per scale row
   const int count = (nslabs - w + WAVES - 1) / WAVES;         // this wave's slabs
   const int iters = (count + UNROLL - 1) / UNROLL;
 
@@ -83,22 +95,25 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qa), static_cast<short>(0), M * K, static_cast<int>(kRsrcWord3));
   // blockwise scales: sa [M][KG] and the rows of sb [ceil(N/128)][KG] of the weight blocks
-  // nb0 .. nb1 this workgroup touches
+  // nb0 .. nb1 this workgroup touches (float32, or UE8M0 bytes in rows of KG4)
   const int nb0 = n0 / kSlab, nb1 = (n0 + rows - 1) / kSlab;
   const __amdgpu_buffer_rsrc_t sar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(sa), static_cast<short>(0), BLOCKWISE ? M * KG * 4 : 0,
+      const_cast<void*>(sa_), static_cast<short>(0), BLOCKWISE ? M * SR : 0,
       static_cast<int>(kRsrcWord3));
   const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(nb0) * KG : 0)), static_cast<short>(0),
-      BLOCKWISE ? (nb1 - nb0 + 1) * KG * 4 : 0, static_cast<int>(kRsrcWord3));
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(sb_) + (BLOCKWISE ? static_cast<int64_t>(nb0) * SR : 0)),
+      static_cast<short>(0), BLOCKWISE ? (nb1 - nb0 + 1) * SR : 0, static_cast<int>(kRsrcWord3));
 
   // operands of this wave's i-th slab; past the wave's share every load reads zeros (the
   // scales too, so such a slab adds 0 * 0 and a non-finite scale elsewhere cannot leak in)
+  // UE8M0: sav / sbv hold the 32-bit words with the slab's scale bytes, slab[u] the slab
   v8i wf[UNROLL][NB], af[UNROLL][MB];
   float sav[UNROLL][MB], sbv[UNROLL][NB];
+  int slab[UNROLL];
   auto fetch = [&](int i, int u) {
     const bool live = i < count;                              // wave-uniform
     const int s = w + i * WAVES;
+    slab[u] = s;
     const int kk = s * kSlab + kq * 32;
     const bool lo_in = live && kk < K, hi_in = live && kk + 16 < K;
 #pragma unroll
@@ -117,12 +132,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
         const int m = 16 * b + r16;
-        const uint32_t soff = static_cast<uint32_t>((m * KG + s) * 4);
+        const uint32_t soff = static_cast<uint32_t>(m * SR + (E8M0 ? (s & ~3) : s * 4));
         sav[u][b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sar, (live && m < M) ? soff : kOOB, 0, 0));
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const uint32_t soff = static_cast<uint32_t>((((n0 + 16 * j) / kSlab - nb0) * KG + s) * 4);
+        const uint32_t soff = static_cast<uint32_t>(((n0 + 16 * j) / kSlab - nb0) * SR + (E8M0 ? (s & ~3) : s * 4));
         sbv[u][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, (live && 16 * j < rows) ? soff : kOOB, 0, 0));
       }
     }
@@ -138,6 +153,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
     for (int b = 0; b < MB; ++b) { af[u][b] = v8i{0, 0, 0, 0, 0, 0, 0, 0}; sav[u][b] = 0.0f; }
 #pragma unroll
     for (int j = 0; j < NB; ++j) { wf[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0}; sbv[u][j] = 0.0f; }
+    slab[u] = 0;
   }
   v4f acc[NB][MB];
 #pragma unroll
@@ -149,7 +165,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
-        if constexpr (BLOCKWISE) {
+        if constexpr (E8M0) {
+          acc[j][b] = mfma_fp8_e8m0(wf[u][j], af[u][b], acc[j][b], e8m0_byte(__float_as_uint(sbv[u][j]), slab[u]),
+                                    e8m0_byte(__float_as_uint(sav[u][b]), slab[u]));
+        } else if constexpr (BLOCKWISE) {
           const float scale = sav[u][b] * sbv[u][j];
           const v4f p = mfma_fp8(wf[u][j], af[u][b], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
@@ -227,10 +246,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
 // lane's 16-term partial.  At the end the 64 lanes' partials of each (m, row) are summed by
 // a butterfly.  The float32 sum is ordered differently from the MFMA path; both are within
 // the product tolerance of the exact sum.
-template <bool BLOCKWISE, int OUT, int MT, int RPW, int UNROLL>
+template <int SM, int OUT, int MT, int RPW, int UNROLL>
 __global__ __launch_bounds__(256) void gemv_valu_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qb,
-    const float* __restrict__ sb, int M, int N, int K, uint16_t* __restrict__ c) {
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c) {
+  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool E8M0 = SM == SM_E8M0;
+  const float* __restrict__ sa = static_cast<const float*>(sa_);
+  const float* __restrict__ sb = static_cast<const float*>(sb_);
   static_assert(MT * RPW <= 64 && 128 % RPW == 0, "one output per lane; a wave's rows share a weight block");
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63;
@@ -239,6 +262,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
   if (row0 >= N) return;                                      // no barrier in this kernel
   const int rows = min(RPW, N - row0);
   const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
+  const int SR = E8M0 ? static_cast<int>(e8m0_row_bytes(KG)) : KG * 4;   // bytes per scale row
   const int nch = (K + 1023) / 1024;
   const int iters = (nch + UNROLL - 1) / UNROLL;
 
@@ -249,16 +273,18 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qa), static_cast<short>(0), M * K, static_cast<int>(kRsrcWord3));
   const __amdgpu_buffer_rsrc_t sar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(sa), static_cast<short>(0), BLOCKWISE ? M * KG * 4 : 0,
+      const_cast<void*>(sa_), static_cast<short>(0), BLOCKWISE ? M * SR : 0,
       static_cast<int>(kRsrcWord3));
   const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(sb + (BLOCKWISE ? static_cast<int64_t>(row0 / kSlab) * KG : 0)),
-      static_cast<short>(0), BLOCKWISE ? KG * 4 : 0, static_cast<int>(kRsrcWord3));
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(sb_) + (BLOCKWISE ? static_cast<int64_t>(row0 / kSlab) * SR : 0)),
+      static_cast<short>(0), BLOCKWISE ? SR : 0, static_cast<int>(kRsrcWord3));
 
   // operands of chunk i in slot u; past the last chunk every load reads zeros (the scales
-  // too, so such a chunk adds 0 * 0)
+  // too, so such a chunk adds 0 * 0).  UE8M0: sav / sbv hold the 32-bit words with the
+  // scale bytes of this lane's slab, gsl[u] that slab.
   v4i wv[UNROLL][RPW], av[UNROLL][MT];
   float sav[UNROLL][MT], sbv[UNROLL];
+  int gsl[UNROLL];
   auto fetch = [&](int i, int u) {
     const int col = i * 1024 + lane * 16;
     const bool in = (i < nch) & (col < K);                   // K % 16 == 0
@@ -270,11 +296,13 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
       av[u][m] = __builtin_amdgcn_raw_buffer_load_b128(ar, (in & (m < M)) ? static_cast<uint32_t>(m * K + col) : kOOB, 0, 0);
     if constexpr (BLOCKWISE) {
       const int g = col >> 7;
+      const int goff = E8M0 ? (g & ~3) : g * 4;
+      gsl[u] = g;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         sav[u][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            sar, (in & (m < M)) ? static_cast<uint32_t>((m * KG + g) * 4) : kOOB, 0, 0));
-      sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, in ? static_cast<uint32_t>(g * 4) : kOOB, 0, 0));
+            sar, (in & (m < M)) ? static_cast<uint32_t>(m * SR + goff) : kOOB, 0, 0));
+      sbv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sbr, in ? static_cast<uint32_t>(goff) : kOOB, 0, 0));
     }
   };
 
@@ -287,6 +315,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m) { av[u][m] = v4i{0, 0, 0, 0}; sav[u][m] = 0.0f; }
     sbv[u] = 0.0f;
+    gsl[u] = 0;
   }
   float acc[MT][RPW];
 #pragma unroll
@@ -316,8 +345,18 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
         float d = BLOCKWISE ? 0.0f : acc[m][r];
 #pragma unroll
         for (int p = 0; p < 8; ++p) d = __builtin_amdgcn_fdot2(wh[p], ah[m][p], d, false);
-        if constexpr (BLOCKWISE) acc[m][r] = __builtin_fmaf(d, sav[u][m] * sbv[u], acc[m][r]);
-        else acc[m][r] = d;
+        if constexpr (E8M0) {
+          // d * 2^(ea - 127) * 2^(eb - 127) in one exact step; a NaN code gives NaN
+          const int ea = e8m0_byte(__float_as_uint(sav[u][m]), gsl[u]);
+          const int eb = e8m0_byte(__float_as_uint(sbv[u]), gsl[u]);
+          const float t = (ea == 0xff || eb == 0xff) ? __uint_as_float(kCanonicalNaN)
+                                                     : __builtin_amdgcn_ldexpf(d, ea + eb - 254);
+          acc[m][r] += t;
+        } else if constexpr (BLOCKWISE) {
+          acc[m][r] = __builtin_fmaf(d, sav[u][m] * sbv[u], acc[m][r]);
+        } else {
+          acc[m][r] = d;
+        }
       }
     }
   };
@@ -356,16 +395,16 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
     c[static_cast<int64_t>(m) * N + row0 + r] = static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * alpha));
 }
 
-template <bool BW, int OUT, int MT, int RPW, int UNROLL>
-void launch_valu_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int BW, int OUT, int MT, int RPW, int UNROLL>
+void launch_valu_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
   const int waves = (N + RPW - 1) / RPW;
   gemv_valu_kernel<BW, OUT, MT, RPW, UNROLL><<<(waves + 3) / 4, 256, 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
 }
 
-template <bool BW, int OUT, int WAVES, int UNROLL, int NB, int MB = 1>
-void launch_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int BW, int OUT, int WAVES, int UNROLL, int NB, int MB = 1>
+void launch_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
               int K, void* c, hipStream_t s) {
   gemv_fp8_kernel<BW, OUT, WAVES, UNROLL, NB, MB><<<(N + 16 * NB - 1) / (16 * NB), WAVES * 64, 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
@@ -374,12 +413,19 @@ void launch_t(const uint8_t* qa, const float* sa, const uint8_t* qb, const float
 // Measured on MI355X with cold weights: one token runs best on the vector-ALU kernel
 // (1 KB row streams); from two tokens on the MFMA kernel, with two row blocks per wave once
 // the activation fragment is worth sharing (M > 4).
-template <bool BW, int OUT>
-void launch_m(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int M, int N,
+template <int BW, int OUT>
+void launch_m(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
               int K, void* c, hipStream_t s) {
   if (M == 1) launch_valu_t<BW, OUT, 1, 2, 4>(qa, sa, qb, sb, M, N, K, c, s);
   else if (M <= 4) launch_t<BW, OUT, 2, 4, 1>(qa, sa, qb, sb, M, N, K, c, s);
   else launch_t<BW, OUT, 4, 2, 2>(qa, sa, qb, sb, M, N, K, c, s);
+}
+
+template <int SM>
+void launch_gemv_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M,
+                   int N, int K, void* c, hipStream_t s) {
+  if (out_dt == DT_BF16) launch_m<SM, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
+  else launch_m<SM, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
@@ -388,15 +434,11 @@ bool gemv_fits(int M, int K) {
   return M >= 1 && M <= 16 && static_cast<int64_t>(K) * 32 < (int64_t{1} << 31);
 }
 
-void launch_gemv(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
-                 const float* sb, int M, int N, int K, void* c, hipStream_t s) {
-  if (blockwise) {
-    if (out_dt == DT_BF16) launch_m<true, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_m<true, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
-  } else {
-    if (out_dt == DT_BF16) launch_m<false, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_m<false, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
-  }
+void launch_gemv(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                 const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (mode == SM_E8M0) launch_gemv_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  else if (mode == SM_BLOCK) launch_gemv_m<SM_BLOCK>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  else launch_gemv_m<SM_TENSOR>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace fp8amax

@@ -6,10 +6,25 @@
 
 namespace fp8amax {
 
+// How a GEMM is scaled (template argument of the GEMM kernels, argument of the launchers):
+//   SM_TENSOR: one float32 scale per operand;
+//   SM_BLOCK:  float32 scales per 1x128 activation group and 128x128 weight block;
+//   SM_E8M0:   the same groups and blocks with UE8M0 scales, one e8m0fnu byte each,
+//              every scale row padded to whole 32-bit words (e8m0_row_bytes).
+enum ScaleMode { SM_TENSOR = 0, SM_BLOCK = 1, SM_E8M0 = 2 };
+
+// Bytes per row of a UE8M0 scale tensor with `groups` scales: four per 32-bit word.
+__host__ __device__ constexpr int64_t e8m0_row_bytes(int64_t groups) { return (groups + 3) & ~int64_t{3}; }
+
 // Fused amax + scale + cast per group (group_rows 1 or 128, group_cols 128).  With
 // write_q = false only the amax grid is written to `out`.
 void launch_groups(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
                    uint8_t* q, float* out, bool write_q, hipStream_t s);
+
+// The same groups and blocks with UE8M0 scales: the codes, and one e8m0fnu byte per group
+// in rows of e8m0_row_bytes(groups per row) bytes whose padding is set to 127.
+void launch_groups_e8m0(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
+                        uint8_t* q, uint8_t* codes, hipStream_t s);
 
 // Whole-tensor amax of n elements into the word `word`.  want_scale = false: the word ends
 // as the float amax.  want_scale = true: the word holds a pending reduction key that
@@ -30,13 +45,13 @@ void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t*
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 
 // Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its
-// launcher.
+// launcher.  sa and sb point at float32 scales, or at e8m0fnu bytes for SM_E8M0.
 bool gemv_fits(int M, int K);
-void launch_gemv(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
-                 const float* sb, int M, int N, int K, void* c, hipStream_t s);
+void launch_gemv(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                 const void* sb, int M, int N, int K, void* c, hipStream_t s);
 
 // Scaled FP8 GEMM, C [M, N] of out_dt (dispatches M <= 16 to the GEMV path).
-void launch_gemm(bool blockwise, int out_dt, const uint8_t* qa, const float* sa, const uint8_t* qb,
-                 const float* sb, int M, int N, int K, void* c, hipStream_t s);
+void launch_gemm(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                 const void* sb, int M, int N, int K, void* c, hipStream_t s);
 
 }  // namespace fp8amax

@@ -69,16 +69,48 @@ __device__ __forceinline__ uint8_t enc1(uint32_t h, float s, float r, bool fast)
   return static_cast<uint8_t>(e4m3_encode(x / s));
 }
 
+// A group's scale from its amax, and the value stored for it: the float32 scale amax / 448,
+// or (E8M0) the power-of-two scale and its e8m0fnu code.
+template <bool E8M0>
+struct GroupScale {
+  float scale;
+  uint32_t code;
+  __device__ __forceinline__ explicit GroupScale(float amax) {
+    if constexpr (E8M0) {
+      code = e8m0_from_amax(amax);
+      scale = e8m0_value(code);
+    } else {
+      scale = scale_from_amax(amax);
+      code = 0;
+    }
+  }
+  // Store the scale of group (row, col) of a grid with `ncols` groups per row: float32
+  // rows are ncols long; UE8M0 rows are `stride` bytes (ncols rounded up to whole 32-bit
+  // words), and the group that ends a row also sets the row's padding bytes to 127 (2^0).
+  __device__ __forceinline__ void store(void* out, int64_t row, int64_t col, int64_t ncols,
+                                        int64_t stride) const {
+    if constexpr (E8M0) {
+      uint8_t* o = static_cast<uint8_t*>(out) + row * stride;
+      o[col] = static_cast<uint8_t>(code);
+      if (col == ncols - 1)
+        for (int64_t p = ncols; p < stride; ++p) o[p] = 127;
+    } else {
+      static_cast<float*>(out)[row * ncols + col] = scale;
+    }
+  }
+};
+
 // ------------------------------------------------------------------------------------
 // Per-token 1x128 groups.  Sixteen lanes (one DPP row) own one group, 8 elements each.
 // Each 16-lane set takes one (row, chunk) pair: `cg` consecutive groups of one row,
 // walked UNROLL groups at a time with all loads issued before the reductions.
 // Vector path: cols % 8 == 0 (a lane's eight elements are all inside or all outside).
-// WRITE_Q = false computes only the amax grid (fp8_amax with 1x128 blocks).
-template <int DT, bool WRITE_Q, int UNROLL>
+// WRITE_Q = false computes only the amax grid (fp8_amax with 1x128 blocks).  E8M0: the
+// scales are UE8M0 codes (bytes) instead of float32.
+template <int DT, bool WRITE_Q, int UNROLL, bool E8M0 = false>
 __global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t nch, int64_t cg,
-    uint8_t* __restrict__ q, float* __restrict__ out) {
+    uint8_t* __restrict__ q, void* __restrict__ out, int64_t sstride) {
   const int64_t gcols = (cols + 127) >> 7;
   const int sub = threadIdx.x & 15;
   const int64_t nsets = rows * nch;
@@ -105,13 +137,14 @@ __global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
       const uint32_t key = max16(key8(v[u]));
       const float amax = amax_from_key<DT>(key);
       if constexpr (WRITE_Q) {
-        const float scale = scale_from_amax(amax);
+        const GroupScale<E8M0> gs(amax);
+        const float scale = gs.scale;
         const bool fast = fast_scale(scale);
         const float r = 1.0f / scale;
         if (col < cols) *reinterpret_cast<uint2*>(q + row * cols + col) = enc8<DT>(v[u], scale, r, fast);
-        if (sub == 0) out[row * gcols + g] = scale;
+        if (sub == 0) gs.store(out, row, g, gcols, sstride);
       } else {
-        if (sub == 0) out[row * gcols + g] = amax;
+        if (sub == 0) static_cast<float*>(out)[row * gcols + g] = amax;
       }
     }
   }
@@ -119,10 +152,10 @@ __global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
 }
 
 // Scalar path for rows whose length is not a multiple of 8: one group per 16-lane set.
-template <int DT, bool WRITE_Q>
+template <int DT, bool WRITE_Q, bool E8M0 = false>
 __global__ __launch_bounds__(kThreads) void group_1x128_scalar_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
-    float* __restrict__ out) {
+    void* __restrict__ out, int64_t sstride) {
   const int64_t gcols = (cols + 127) >> 7;
   const int64_t ngroups = rows * gcols;
   const int sub = threadIdx.x & 15;
@@ -142,15 +175,16 @@ __global__ __launch_bounds__(kThreads) void group_1x128_scalar_kernel(
   const uint32_t key = max16(m);
   const float amax = amax_from_key<DT>(key);
   if constexpr (WRITE_Q) {
-    const float scale = scale_from_amax(amax);
+    const GroupScale<E8M0> gs(amax);
+    const float scale = gs.scale;
     const bool fast = fast_scale(scale);
     const float r = 1.0f / scale;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (col0 + i < cols) q[row * cols + col0 + i] = enc1<DT>(h[i], scale, r, fast);
-    if (sub == 0) out[g] = scale;
+    if (sub == 0) gs.store(out, row, gc, gcols, sstride);
   } else {
-    if (sub == 0) out[g] = amax;
+    if (sub == 0) static_cast<float*>(out)[g] = amax;
   }
   }
 }
@@ -159,10 +193,10 @@ __global__ __launch_bounds__(kThreads) void group_1x128_scalar_kernel(
 // 128x128 weight blocks: one workgroup per block.  Thread t owns columns
 // [8*(t%16), +8) of rows t/16 + 16*i, i = 0..7: eight 16-byte loads held in registers
 // through the block-wide reduction, then cast and stored.  VEC: cols % 8 == 0.
-template <int DT, bool WRITE_Q, bool VEC>
+template <int DT, bool WRITE_Q, bool VEC, bool E8M0 = false>
 __global__ __launch_bounds__(kThreads) void block_128x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
-    float* __restrict__ out) {
+    void* __restrict__ out, int64_t sstride) {
   __shared__ uint32_t wave_max[kThreads / 64];
   const int64_t bcols = (cols + 127) >> 7;
   const int64_t nblocks = ((rows + 127) >> 7) * bcols;
@@ -196,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void block_128x128_kernel(
   __syncthreads();                                 // wave_max is rewritten next iteration
   const float amax = amax_from_key<DT>(m);
   if constexpr (WRITE_Q) {
-    const float scale = scale_from_amax(amax);
+    const GroupScale<E8M0> gs(amax);
+    const float scale = gs.scale;
     const bool fast = fast_scale(scale);
     const float r = 1.0f / scale;
 #pragma unroll
@@ -213,9 +248,9 @@ __global__ __launch_bounds__(kThreads) void block_128x128_kernel(
           if (col + e < cols) q[row * cols + col + e] = static_cast<uint8_t>(b[e >> 2] >> (8 * (e & 3)));
       }
     }
-    if (t == 0) out[blk] = scale;
+    if (t == 0) gs.store(out, br, bc, bcols, sstride);
   } else {
-    if (t == 0) out[blk] = amax;
+    if (t == 0) static_cast<float*>(out)[blk] = amax;
   }
   }
 }
@@ -363,9 +398,9 @@ constexpr int64_t kGroupCap = 256 * 256;     // group/block kernels loop beyond 
 constexpr int kGroupUnroll = 2;
 constexpr int64_t kGroupSetsPerCu = 64;
 
-template <int DT, bool WRITE_Q, int UNROLL>
+template <int DT, bool WRITE_Q, int UNROLL, bool E8M0 = false>
 void launch_group_vec(const uint16_t* xp, int64_t rows, int64_t cols, int64_t sets_per_cu, uint8_t* q,
-                      float* out, hipStream_t s) {
+                      void* out, int64_t sstride, hipStream_t s) {
   const int64_t gcols = (cols + 127) / 128;
   const int64_t ngroups = rows * gcols;
   const int64_t target_sets = 256 * sets_per_cu;
@@ -373,33 +408,33 @@ void launch_group_vec(const uint16_t* xp, int64_t rows, int64_t cols, int64_t se
   cg = ((cg + UNROLL - 1) / UNROLL) * UNROLL;
   const int64_t nch = (gcols + cg - 1) / cg;
   const unsigned grid = grid_for(rows * nch, 16, kGroupCap);
-  group_1x128_vec_kernel<DT, WRITE_Q, UNROLL><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out);
+  group_1x128_vec_kernel<DT, WRITE_Q, UNROLL, E8M0><<<grid, kThreads, 0, s>>>(xp, rows, cols, nch, cg, q, out, sstride);
 }
 
-template <int DT>
+template <int DT, bool E8M0>
 void launch_groups_t(const void* x, int64_t rows, int64_t cols, int32_t group_rows, uint8_t* q,
-                     float* out, bool write_q, hipStream_t s) {
+                     void* out, bool write_q, int64_t sstride, hipStream_t s) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const bool vec = (cols % 8) == 0;
   if (group_rows == 1) {
     const int64_t gcols = (cols + 127) / 128;
     const int64_t ngroups = rows * gcols;
     if (vec) {
-      if (write_q) launch_group_vec<DT, true, kGroupUnroll>(xp, rows, cols, kGroupSetsPerCu, q, out, s);
-      else launch_group_vec<DT, false, kGroupUnroll>(xp, rows, cols, kGroupSetsPerCu, q, out, s);
+      if (write_q) launch_group_vec<DT, true, kGroupUnroll, E8M0>(xp, rows, cols, kGroupSetsPerCu, q, out, sstride, s);
+      else launch_group_vec<DT, false, kGroupUnroll>(xp, rows, cols, kGroupSetsPerCu, q, out, sstride, s);
     } else {
       const unsigned grid = grid_for(ngroups, 16, kGroupCap);
-      if (write_q) group_1x128_scalar_kernel<DT, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
-      else group_1x128_scalar_kernel<DT, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+      if (write_q) group_1x128_scalar_kernel<DT, true, E8M0><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out, sstride);
+      else group_1x128_scalar_kernel<DT, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out, sstride);
     }
   } else {
     const unsigned grid = grid_for(((rows + 127) / 128) * ((cols + 127) / 128), 1, kGroupCap);
     if (vec) {
-      if (write_q) block_128x128_kernel<DT, true, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
-      else block_128x128_kernel<DT, false, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+      if (write_q) block_128x128_kernel<DT, true, true, E8M0><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out, sstride);
+      else block_128x128_kernel<DT, false, true><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out, sstride);
     } else {
-      if (write_q) block_128x128_kernel<DT, true, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
-      else block_128x128_kernel<DT, false, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out);
+      if (write_q) block_128x128_kernel<DT, true, false, E8M0><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out, sstride);
+      else block_128x128_kernel<DT, false, false><<<grid, kThreads, 0, s>>>(xp, rows, cols, q, out, sstride);
     }
   }
 }
@@ -426,8 +461,16 @@ void launch_tensor_reduce_t(const void* x, int64_t n, float* word, bool want_sca
 
 void launch_groups(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
                    uint8_t* q, float* out, bool write_q, hipStream_t s) {
-  if (dt == DT_BF16) launch_groups_t<DT_BF16>(x, rows, cols, group_rows, q, out, write_q, s);
-  else launch_groups_t<DT_F16>(x, rows, cols, group_rows, q, out, write_q, s);
+  const int64_t gc = (cols + 127) / 128;
+  if (dt == DT_BF16) launch_groups_t<DT_BF16, false>(x, rows, cols, group_rows, q, out, write_q, gc, s);
+  else launch_groups_t<DT_F16, false>(x, rows, cols, group_rows, q, out, write_q, gc, s);
+}
+
+void launch_groups_e8m0(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
+                        uint8_t* q, uint8_t* codes, hipStream_t s) {
+  const int64_t row_bytes = e8m0_row_bytes((cols + 127) / 128);
+  if (dt == DT_BF16) launch_groups_t<DT_BF16, true>(x, rows, cols, group_rows, q, codes, true, row_bytes, s);
+  else launch_groups_t<DT_F16, true>(x, rows, cols, group_rows, q, codes, true, row_bytes, s);
 }
 
 void launch_tensor_reduce(int dt, const void* x, int64_t n, float* word, bool want_scale,

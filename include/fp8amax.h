@@ -138,6 +138,39 @@ fp8_status_t fp8_gemm_scaled_blockwise(const uint8_t* qa, const float* sa,
                                        void* c, fp8_dtype_t out_dt, void* stream);
 
 /*
+ * fp8_quantize_per_token_group_ue8m0 - fp8_quantize_per_token_group with UE8M0 scales
+ * ("FP8 chi tiết", the UE8M0 scale format section: scales kept as packed float8_e8m0fnu
+ * bytes instead of float32).  A group's scale is the smallest power of two not below
+ * amax/448, clamped to 2^-127 .. 2^127 (amax 0 -> 2^0; NaN or infinite amax -> NaN), stored
+ * as one e8m0fnu byte b (value 2^(b - 127), b = 255 is NaN); q = e4m3(x / scale).
+ *   scales : uint8 output [ceil(rows/group_rows), G4] row-major, where G4 is
+ *            ceil(cols/group_cols) rounded up to a multiple of 4 (four scales per 32-bit
+ *            word); the padding bytes at the end of each row are set to 127.
+ * Other arguments and errors: as fp8_quantize_per_token_group (scales need 4-byte
+ * alignment).
+ */
+fp8_status_t fp8_quantize_per_token_group_ue8m0(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                                int32_t group_rows, int32_t group_cols,
+                                                uint8_t* q, uint8_t* scales, void* stream);
+
+/*
+ * fp8_gemm_scaled_blockwise_ue8m0 - fp8_gemm_scaled_blockwise with UE8M0 scales (same
+ * section): per 128-wide K slab g,
+ *   C = out( sum_g 2^(sa[m,g] - 127) * 2^(sb[n/128,g] - 127) * (sum_{k in slab g} qa[m,k] * qb[n,k]) )
+ *   sa : uint8 e8m0fnu [M, G4];  sb : uint8 e8m0fnu [ceil(N/128), G4], with G4 = K/128
+ *        rounded up to a multiple of 4, the layout fp8_quantize_per_token_group_ue8m0
+ *        writes (the padding bytes are read with their word and ignored).
+ * The scales are applied inside the gfx950 scaled FP8 MFMA, so each slab's product is
+ * added to the float32 accumulator directly.  A scale byte of 255 makes the affected
+ * outputs NaN.  Requires K % 128 == 0 and K > 0; M == 0 or N == 0 returns FP8_OK.
+ * qa, qb and c need 16-byte alignment, sa and sb 4-byte alignment.
+ */
+fp8_status_t fp8_gemm_scaled_blockwise_ue8m0(const uint8_t* qa, const uint8_t* sa,
+                                             const uint8_t* qb, const uint8_t* sb,
+                                             int64_t M, int64_t N, int64_t K,
+                                             void* c, fp8_dtype_t out_dt, void* stream);
+
+/*
  * fp8_debug_cast_f32 - test hook: q[i] = e4m3(v[i]) with the same device encoder the
  * quantizers use (saturating round to nearest even; NaN -> 0x7F).  v is float32 [n],
  * q is uint8 [n].  n == 0 returns FP8_OK.

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(L):
     names = header_functions()
     assert set(names) == {"fp8_status_string", "fp8_amax", "fp8_quantize_per_tensor",
                           "fp8_quantize_per_token_group", "fp8_gemm_scaled_tensorwise",
-                          "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32"}
+                          "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
+                          "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -42,7 +43,8 @@ def test_status_strings(L):
     assert L.fp8_status_string(99) == b"unknown fp8_status_t"
 
 
-@pytest.mark.parametrize("fn", ["fp8_gemm_scaled_tensorwise", "fp8_gemm_scaled_blockwise"])
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled_tensorwise", "fp8_gemm_scaled_blockwise",
+                                "fp8_gemm_scaled_blockwise_ue8m0"])
 def test_gemm_validation(L, fn):
     f = getattr(L, fn)
     good = (A16, A16, A16, A16)
@@ -59,6 +61,20 @@ def test_gemm_validation(L, fn):
     assert f(A16, A16, A16, A16, 4, 4, 128, MIS, 0, None) == ALIGN
     assert f(A16, A16 + 2, A16, A16, 4, 4, 128, A16, 0, None) == ALIGN   # float pointer needs 4 B
     assert f(*good, 2 ** 31, 4, 128, A16, 0, None) == LARGE
+
+
+@pytest.mark.parametrize("fn", ["fp8_quantize_per_token_group", "fp8_quantize_per_token_group_ue8m0"])
+def test_group_quantize_validation(L, fn):
+    q = getattr(L, fn)
+    assert q(A16, 0, 4, 256, 2, 128, A16, A16, None) == SHAPE      # unsupported group
+    assert q(A16, 0, 4, 256, 1, 64, A16, A16, None) == SHAPE
+    assert q(A16, 0, -4, 256, 1, 128, A16, A16, None) == SHAPE
+    assert q(A16, 2, 4, 256, 1, 128, A16, A16, None) == DTYPE
+    assert q(A16, 0, 0, 256, 1, 128, None, None, None) == OK        # empty
+    assert q(None, 0, 4, 256, 1, 128, A16, A16, None) == NULLP
+    assert q(MIS, 0, 4, 256, 128, 128, A16, A16, None) == ALIGN
+    assert q(A16, 0, 4, 256, 128, 128, MIS, A16, None) == ALIGN
+    assert q(A16, 0, 4, 256, 128, 128, A16, A16 + 2, None) == ALIGN   # scale rows are 4-byte words
 
 
 def test_quantize_validation(L):
