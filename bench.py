@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--m", type=int, default=None, help="M variant of the workload (default: largest)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--scale-fmt", choices=["float32", "ue8m0"], default="float32",
+                   help="blockwise workloads: float32 scales (amax/448) or UE8M0 power-of-two "
+                        "scale bytes on the scaled MFMA")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the hot path, run a plain device copy of this many MiB "
                         "(the known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -61,7 +64,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, M):
+def traffic_key(workload, M, scale_fmt="float32"):
+    return f"{workload}/M={M}" + ("/ue8m0" if scale_fmt == "ue8m0" else "")
+
+
+def measured_traffic(workload, M, scale_fmt="float32"):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, or None when
     there is no entry for this workload or the kernel sources changed since it was taken."""
     import json as _json
@@ -70,7 +77,7 @@ def measured_traffic(workload, M):
             table = _json.load(f)
     except (OSError, ValueError):
         return None
-    e = table.get(f"{workload}/M={M}")
+    e = table.get(traffic_key(workload, M, scale_fmt))
     if not e or e.get("kernel_source_sha") != kernel_source_hash():
         return None
     return e.get("traffic_bytes_per_launch")
@@ -94,12 +101,16 @@ def copy_reference(mib, steps):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def algorithmic_bytes(w, M):
+def algorithmic_bytes(w, M, scale_fmt="float32"):
     """ABI-level bytes of one step: A read as bf16, qA written and read, scales, W read
-    as FP8 with its scales, C written; plus B's quantize when it runs every call."""
+    as FP8 with its scales, C written; plus B's quantize when it runs every call.  UE8M0
+    scales are one byte each in rows padded to four bytes."""
     N, K = w.n, w.k
     if w.mode == "tensorwise":
         sa_bytes, sb_bytes = 4, 4
+    elif scale_fmt == "ue8m0":
+        g4 = (K // 128 + 3) // 4 * 4
+        sa_bytes, sb_bytes = M * g4, -(-N // 128) * g4
     else:
         sa_bytes, sb_bytes = M * (K // 128) * 4, -(-N // 128) * (K // 128) * 4
     quant_a = 2 * M * K + M * K + sa_bytes
@@ -108,15 +119,18 @@ def algorithmic_bytes(w, M):
     return quant_a + gemm + quant_b, gemm
 
 
-def cpu_baseline(w, a_bits, b_bits, budget_s=20.0):
+def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32"):
     """The oracle's quantize(A) + scaled GEMM on the host, on a row sample of A sized to
     roughly `budget_s` seconds; returns TFLOP/s (float64 arithmetic)."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
     M, N, K = a_bits.shape[0], w.n, w.k
+    ue8m0 = scale_fmt == "ue8m0"
     if w.mode == "tensorwise":
         qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
+    elif ue8m0:
+        qb, sb = oracle.quantize_groups_ue8m0(b_bits, "bf16", 128, 128)
     else:
         qb, sb = oracle.quantize_groups(b_bits, "bf16", 128, 128)
     rows = M
@@ -130,6 +144,9 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0):
             if w.quantize_b_per_call:
                 qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
             oracle.gemm_tensorwise_ref(qa, sa, qb, sb)
+        elif ue8m0:
+            qa, sa = oracle.quantize_groups_ue8m0(a, "bf16", 1, 128)
+            oracle.gemm_blockwise_ue8m0_ref(qa, sa, qb, sb)
         else:
             qa, sa = oracle.quantize_groups(a, "bf16", 1, 128)
             oracle.gemm_blockwise_ref(qa, sa, qb, sb)
@@ -144,7 +161,7 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0):
     best = min(runs)
     flops = 2.0 * rows * N * K
     return {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle quantize(A[{rows},{K}]) + {w.mode} GEMM with W[{N},{K}], best of "
+            "sample": f"oracle quantize(A[{rows},{K}]) + {w.mode}{' UE8M0' if ue8m0 else ''} GEMM with W[{N},{K}], best of "
                       f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
 
 
@@ -172,11 +189,16 @@ def main():
     a_bits, b_bits = wl.make_inputs(args.workload, M)
     out_dtype = torch.float16 if w.out_dtype == "f16" else torch.bfloat16
     blockwise = w.mode == "blockwise"
+    ue8m0 = args.scale_fmt == "ue8m0"
+    if ue8m0 and not blockwise:
+        print(f"--scale-fmt ue8m0 needs a blockwise workload; {args.workload} is {w.mode}", file=sys.stderr)
+        sys.exit(2)
 
     a0 = wl.bits_to_tensor(a_bits, device=dev)
     b0 = wl.bits_to_tensor(b_bits, device=dev)
     if blockwise:
-        qb0, sb0 = fp8.fp8_quantize_per_token_group(b0, 128, 128)
+        quant_groups = fp8.fp8_quantize_per_token_group_ue8m0 if ue8m0 else fp8.fp8_quantize_per_token_group
+        qb0, sb0 = quant_groups(b0, 128, 128)
     else:
         qb0, sb0 = fp8.fp8_quantize_per_tensor(b0)
 
@@ -191,7 +213,8 @@ def main():
             s["qb"], s["sb"] = qb0.clone(), sb0.clone()
         if blockwise:
             s["qa"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            s["sa"] = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+            s["sa"] = (torch.empty((M, fp8.e8m0_row_bytes(K // 128)), dtype=torch.uint8, device=dev) if ue8m0
+                       else torch.empty((M, K // 128), dtype=torch.float32, device=dev))
         else:
             s["qa"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
             s["sa"] = torch.empty((1,), dtype=torch.float32, device=dev)
@@ -203,7 +226,7 @@ def main():
 
     def quantize(s):
         if blockwise:
-            fp8.fp8_quantize_per_token_group(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
+            quant_groups(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
         else:
             fp8.fp8_quantize_per_tensor(s["a"], q=s["qa"], scale=s["sa"])
             if w.quantize_b_per_call:
@@ -211,7 +234,8 @@ def main():
 
     def gemm(s):
         if blockwise:
-            fp8.fp8_gemm_scaled_blockwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
+            gemm_blockwise = fp8.fp8_gemm_scaled_blockwise_ue8m0 if ue8m0 else fp8.fp8_gemm_scaled_blockwise
+            gemm_blockwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
         else:
             fp8.fp8_gemm_scaled_tensorwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
 
@@ -273,7 +297,7 @@ def main():
     gemm_ms = gs.elapsed_time(ge) / (gemm_reps * R)
 
     flops = 2.0 * M * N * K
-    step_bytes, gemm_bytes = algorithmic_bytes(w, M)
+    step_bytes, gemm_bytes = algorithmic_bytes(w, M, args.scale_fmt)
     decode = M <= 16
     if decode:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -291,20 +315,21 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, M)
+    roof["traffic"] = measured_traffic(args.workload, M, args.scale_fmt)
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K_steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "scaling": w.mode,
+                   "scale_fmt": args.scale_fmt if blockwise else "float32",
                    "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
                    "gemm_ms": round(gemm_ms, 6), "host_s": round(host_s, 4),
                    "step_bytes": step_bytes},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits)
+        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scale_fmt=args.scale_fmt)
     print(json.dumps(result), flush=True)
 
 
