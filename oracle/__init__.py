@@ -27,6 +27,11 @@ It is a plain, slow, obviously correct restatement of what the pages define:
   with the decoded scales.  Source: "FP8 chi tiết", section on the UE8M0 scale
   format.
 
+* ``delayed`` - static scaling (a scale fixed in advance; saturation) and the
+  delayed-scaling amax history (max over the window, times 2^margin, every
+  `interval` steps).  Source: the task page's DelayedScaling recipe and calibration
+  step.
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
 pages print (tests/golden), closed forms, brute force over all 256 codes, exact
 rational arithmetic and library special cases.  No function is "parity
@@ -45,6 +50,7 @@ from .gemm import (gemm_tensorwise_ref, gemm_blockwise_ref, bound_tensorwise,
                    bound_blockwise, output_ulp, check_gemm)
 from .ue8m0 import (e8m0_decode, e8m0_from_amax, quantize_groups_ue8m0,
                     gemm_blockwise_ue8m0_ref, bound_blockwise_ue8m0)
+from .delayed import quantize_static, delayed_scale_from_history, delayed_step
 
 __all__ = [
     "E4M3_MAX", "decode_e4m3", "positive_values", "encode_e4m3", "nonneg_breakpoints",
@@ -53,5 +59,5 @@ __all__ = [
     "gemm_tensorwise_ref", "gemm_blockwise_ref", "bound_tensorwise", "bound_blockwise",
     "output_ulp", "check_gemm",
     "e8m0_decode", "e8m0_from_amax", "quantize_groups_ue8m0", "gemm_blockwise_ue8m0_ref",
-    "bound_blockwise_ue8m0",
+    "bound_blockwise_ue8m0", "quantize_static", "delayed_scale_from_history", "delayed_step",
 ]
