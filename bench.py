@@ -31,6 +31,9 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "tinyllama_upproj_prefill"
 ROTATION_BYTES = 1 << 30
+DELAYED_HISTORY = 16          # amax history length of the delayed recipe (the pages give none)
+DELAYED_INTERVAL = 4          # the recipe's interval and margin
+DELAYED_MARGIN = 0
 
 
 def parse():
@@ -41,6 +44,10 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--m", type=int, default=None, help="M variant of the workload (default: largest)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--act-scaling", choices=["dynamic", "delayed"], default="dynamic",
+                   help="per-tensor workloads: scale from this step's amax (dynamic), or the "
+                        "delayed-scaling recipe (static cast with the scale left by the amax "
+                        "history; margin 0, interval 4)")
     p.add_argument("--scale-fmt", choices=["float32", "ue8m0"], default="float32",
                    help="blockwise workloads: float32 scales (amax/448) or UE8M0 power-of-two "
                         "scale bytes on the scaled MFMA")
@@ -101,10 +108,11 @@ def copy_reference(mib, steps):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def algorithmic_bytes(w, M, scale_fmt="float32"):
+def algorithmic_bytes(w, M, scale_fmt="float32", act_scaling="dynamic"):
     """ABI-level bytes of one step: A read as bf16, qA written and read, scales, W read
     as FP8 with its scales, C written; plus B's quantize when it runs every call.  UE8M0
-    scales are one byte each in rows padded to four bytes."""
+    scales are one byte each in rows padded to four bytes.  Delayed scaling adds, per
+    delayed tensor, the recorded amax word and the update's history, step and scale."""
     N, K = w.n, w.k
     if w.mode == "tensorwise":
         sa_bytes, sb_bytes = 4, 4
@@ -116,17 +124,30 @@ def algorithmic_bytes(w, M, scale_fmt="float32"):
     quant_a = 2 * M * K + M * K + sa_bytes
     gemm = M * K + sa_bytes + N * K + sb_bytes + 2 * M * N
     quant_b = (2 * N * K + N * K + sb_bytes) if w.quantize_b_per_call else 0
+    if act_scaling == "delayed":
+        update = 4 + DELAYED_HISTORY * 4 + 4 + 4 + 4 + 4 + 4       # acc rw, history, step rw, scale
+        quant_a += 4 + update
+        quant_b += (4 + update) if w.quantize_b_per_call else 0
     return quant_a + gemm + quant_b, gemm
 
 
-def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32"):
+def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32", act_scaling="dynamic"):
     """The oracle's quantize(A) + scaled GEMM on the host, on a row sample of A sized to
-    roughly `budget_s` seconds; returns TFLOP/s (float64 arithmetic)."""
+    roughly `budget_s` seconds; returns TFLOP/s (float64 arithmetic).  With delayed
+    scaling the step is the oracle's static cast with the history's scale, its history
+    update, and the GEMM."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
     M, N, K = a_bits.shape[0], w.n, w.k
     ue8m0 = scale_fmt == "ue8m0"
+    delayed = act_scaling == "delayed"
+    if delayed:
+        hist, step_a, scale_a = np.zeros(DELAYED_HISTORY, np.float32), 0, np.float32(1)
+        amax_a = oracle.amax_per_tensor(oracle.input_to_f32(a_bits, "bf16"))
+        for _ in range(DELAYED_INTERVAL):                      # reach the recipe's steady state
+            hist, step_a, scale_a = oracle.delayed_step(hist, step_a, scale_a, amax_a, DELAYED_INTERVAL,
+                                                        DELAYED_MARGIN)
     if w.mode == "tensorwise":
         qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
     elif ue8m0:
@@ -139,7 +160,13 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32"):
     while True:
         a = a_bits[:rows]
         t0 = time.perf_counter()
-        if w.mode == "tensorwise":
+        if w.mode == "tensorwise" and delayed:
+            qa, amax = oracle.quantize_static(a, "bf16", scale_a)
+            oracle.delayed_step(hist, step_a, scale_a, amax, DELAYED_INTERVAL, DELAYED_MARGIN)
+            if w.quantize_b_per_call:
+                qb, _ = oracle.quantize_static(b_bits, "bf16", sb)
+            oracle.gemm_tensorwise_ref(qa, scale_a, qb, sb)
+        elif w.mode == "tensorwise":
             qa, sa = oracle.quantize_per_tensor(a, "bf16")
             if w.quantize_b_per_call:
                 qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
@@ -161,7 +188,8 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32"):
     best = min(runs)
     flops = 2.0 * rows * N * K
     return {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle quantize(A[{rows},{K}]) + {w.mode}{' UE8M0' if ue8m0 else ''} GEMM with W[{N},{K}], best of "
+            "sample": f"oracle {'delayed-scaling ' if delayed else ''}quantize(A[{rows},{K}]) + "
+                      f"{w.mode}{' UE8M0' if ue8m0 else ''} GEMM with W[{N},{K}], best of "
                       f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
 
 
@@ -193,6 +221,17 @@ def main():
     if ue8m0 and not blockwise:
         print(f"--scale-fmt ue8m0 needs a blockwise workload; {args.workload} is {w.mode}", file=sys.stderr)
         sys.exit(2)
+    delayed = args.act_scaling == "delayed"
+    if delayed and blockwise:
+        print(f"--act-scaling delayed is per-tensor scaling; {args.workload} is {w.mode}", file=sys.stderr)
+        sys.exit(2)
+    ds_a = ds_b = None
+    if delayed:
+        # one delayed-scaling state per quantized tensor, shared by the rotation sets: the
+        # sets are successive inputs of the same layer
+        ds_a = fp8.DelayedScaling(DELAYED_HISTORY, DELAYED_INTERVAL, DELAYED_MARGIN, device=dev)
+        if w.quantize_b_per_call:
+            ds_b = fp8.DelayedScaling(DELAYED_HISTORY, DELAYED_INTERVAL, DELAYED_MARGIN, device=dev)
 
     a0 = wl.bits_to_tensor(a_bits, device=dev)
     b0 = wl.bits_to_tensor(b_bits, device=dev)
@@ -227,6 +266,10 @@ def main():
     def quantize(s):
         if blockwise:
             quant_groups(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
+        elif delayed:
+            ds_a.quantize(s["a"], q=s["qa"])
+            if ds_b is not None:
+                ds_b.quantize(s["b"], q=s["qb"])
         else:
             fp8.fp8_quantize_per_tensor(s["a"], q=s["qa"], scale=s["sa"])
             if w.quantize_b_per_call:
@@ -236,16 +279,25 @@ def main():
         if blockwise:
             gemm_blockwise = fp8.fp8_gemm_scaled_blockwise_ue8m0 if ue8m0 else fp8.fp8_gemm_scaled_blockwise
             gemm_blockwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
+        elif delayed:
+            fp8.fp8_gemm_scaled_tensorwise(s["qa"], ds_a.scale, s["qb"], ds_b.scale if ds_b else s["sb"],
+                                           out=s["c"])
         else:
             fp8.fp8_gemm_scaled_tensorwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
 
     def step(s):
         quantize(s)
         gemm(s)
+        if delayed:                         # the scale for the next step
+            ds_a.update()
+            if ds_b is not None:
+                ds_b.update()
 
-    # eager warm-up (first launches, lazy initialisation), then one eager reference output
-    for i in range(max(1, args.warmup)):
+    # eager warm-up (first launches, lazy initialisation; with delayed scaling at least two
+    # intervals, so the scale has reached its steady state), then one eager reference output
+    for i in range(max(1, args.warmup, 2 * DELAYED_INTERVAL if delayed else 1)):
         step(sets[i % R])
+    step(sets[0])
     torch.cuda.synchronize()
     ref_c = sets[0]["c"].clone()
 
@@ -297,7 +349,7 @@ def main():
     gemm_ms = gs.elapsed_time(ge) / (gemm_reps * R)
 
     flops = 2.0 * M * N * K
-    step_bytes, gemm_bytes = algorithmic_bytes(w, M, args.scale_fmt)
+    step_bytes, gemm_bytes = algorithmic_bytes(w, M, args.scale_fmt, args.act_scaling)
     decode = M <= 16
     if decode:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -323,13 +375,18 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "scaling": w.mode,
                    "scale_fmt": args.scale_fmt if blockwise else "float32",
+                   "act_scaling": args.act_scaling if not blockwise else "dynamic",
                    "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
                    "gemm_ms": round(gemm_ms, 6), "host_s": round(host_s, 4),
                    "step_bytes": step_bytes},
         "roofline": roof,
     }
+    if delayed:
+        result["config"].update({"history": DELAYED_HISTORY, "interval": DELAYED_INTERVAL,
+                                 "margin": DELAYED_MARGIN})
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scale_fmt=args.scale_fmt)
+        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scale_fmt=args.scale_fmt,
+                                              act_scaling=args.act_scaling)
     print(json.dumps(result), flush=True)
 
 

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "fp8_gemm_scaled_blockwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_quantize_per_token_group_ue8m0": ([_P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "fp8_gemm_scaled_blockwise_ue8m0": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "fp8_quantize_static": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "fp8_delayed_scaling_update": ([_P, _I32, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
 }
 
@@ -233,6 +235,61 @@ def fp8_gemm_scaled_blockwise_ue8m0(qa, sa, qb, sb, out_dtype=torch.bfloat16, ou
             raise ValueError(f"UE8M0 scales must be [{M}, {g4}] and [{-(-N // 128)}, {g4}], "
                              f"got {tuple(sa.shape)} and {tuple(sb.shape)}")
     return _gemm("fp8_gemm_scaled_blockwise_ue8m0", qa, sa, qb, sb, out_dtype, out, torch.uint8)
+
+
+def fp8_quantize_static(x, scale, q=None, amax_acc=None):
+    """q = e4m3(x / scale) with a given float32 [1] device scale (static or delayed scaling),
+    saturating; if amax_acc (uint32 [1], or int32 viewed as such) is given, the tensor's amax
+    is folded into it for fp8_delayed_scaling_update.  Returns q."""
+    x = _as_2d(x)
+    _need_cuda(x, scale)
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise TypeError("scale must be one float32 value on the device")
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    _need_cuda(q)
+    acc = None
+    if amax_acc is not None:
+        _need_cuda(amax_acc)
+        if amax_acc.element_size() != 4 or amax_acc.numel() != 1:
+            raise TypeError("amax_acc must be one 32-bit word on the device")
+        acc = ctypes.c_void_p(amax_acc.data_ptr())
+    _check("fp8_quantize_static",
+           lib().fp8_quantize_static(_ptr(x), _dt(x), R, C, ctypes.c_void_p(scale.data_ptr()), _ptr(q),
+                                     acc, _stream(x)))
+    return q
+
+
+class DelayedScaling:
+    """Device-resident delayed-scaling state: history float32 [len] (a ring), the amax
+    accumulator (int32 storage of the uint32 word), the step count (int32) and the scale
+    (float32 [1], initially `init_scale`)."""
+
+    def __init__(self, history_len, interval, margin=0, init_scale=1.0, device="cuda"):
+        self.history = torch.zeros(history_len, dtype=torch.float32, device=device)
+        self.amax_acc = torch.zeros(1, dtype=torch.int32, device=device)
+        self.step = torch.zeros(1, dtype=torch.int32, device=device)
+        self.scale = torch.full((1,), float(init_scale), dtype=torch.float32, device=device)
+        self.interval, self.margin = int(interval), int(margin)
+
+    def quantize(self, x, q=None):
+        """Cast x with the current scale and record its amax."""
+        return fp8_quantize_static(x, self.scale, q=q, amax_acc=self.amax_acc)
+
+    def update(self):
+        """Push the recorded amax into the history; refresh the scale every interval steps."""
+        fp8_delayed_scaling_update(self.history, self.amax_acc, self.step, self.interval, self.margin,
+                                   self.scale)
+
+
+def fp8_delayed_scaling_update(history, amax_acc, step, interval, margin, scale):
+    _need_cuda(history, amax_acc, step, scale)
+    _check("fp8_delayed_scaling_update",
+           lib().fp8_delayed_scaling_update(ctypes.c_void_p(history.data_ptr()), history.numel(),
+                                            ctypes.c_void_p(amax_acc.data_ptr()),
+                                            ctypes.c_void_p(step.data_ptr()), interval, margin,
+                                            ctypes.c_void_p(scale.data_ptr()), _stream(history)))
 
 
 def fp8_debug_cast_f32(v, q=None):

@@ -147,6 +147,34 @@ fp8_status_t fp8_gemm_scaled_blockwise_ue8m0(const uint8_t* qa, const uint8_t* s
   return gemm_common(fp8amax::SM_E8M0, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
 }
 
+fp8_status_t fp8_quantize_static(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                 const float* scale, uint8_t* q, uint32_t* amax_acc, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  const int64_t n = rows * cols;
+  if (n == 0) return FP8_OK;
+  if (!x || !q || !scale) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || (amax_acc && !aligned4(amax_acc)))
+    return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_tensor_static(static_cast<int>(dt), x, n, scale, q, amax_acc,
+                                static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+fp8_status_t fp8_delayed_scaling_update(float* history, int32_t len, uint32_t* amax_acc, int32_t* step,
+                                        int32_t interval, int32_t margin, float* scale, void* stream) {
+  if (len < 1 || interval < 1 || margin < -126 || margin > 126) return FP8_ERR_BAD_SHAPE;
+  if (!history || !amax_acc || !step || !scale) return FP8_ERR_NULL_POINTER;
+  if (!aligned4(history) || !aligned4(amax_acc) || !aligned4(step) || !aligned4(scale))
+    return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_delayed_update(history, len, amax_acc, step, interval, margin, scale,
+                                 static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
 fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* stream) {
   if (n < 0) return FP8_ERR_BAD_SHAPE;
   if (n > kMaxElems) return FP8_ERR_TOO_LARGE;

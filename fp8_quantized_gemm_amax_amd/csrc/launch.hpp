@@ -42,6 +42,15 @@ void launch_tensor_quantize(int dt, const void* x, int64_t n, float* scale, uint
 void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t* q,
                         hipStream_t s);
 
+// Static scaling: q[i] = e4m3(x[i] / *scale) for n > 0 elements in one pass; with amax_acc
+// the tensor's amax is folded into *amax_acc (float bits, atomic max).
+void launch_tensor_static(int dt, const void* x, int64_t n, const float* scale, uint8_t* q,
+                          uint32_t* amax_acc, hipStream_t s);
+
+// One delayed-scaling step on device-resident state (see fp8_delayed_scaling_update).
+void launch_delayed_update(float* history, int len, uint32_t* amax_acc, int* step, int interval,
+                           int margin, float* scale, hipStream_t s);
+
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 
 // Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its

@@ -327,6 +327,144 @@ __global__ __launch_bounds__(kThreads) void tensor_cast_kernel(const uint16_t* _
   for (int64_t j = (nvec << 3) + tid; j < n; j += stride) q[j] = enc1<DT>(x[j], scale, r, fast);
 }
 
+// ------------------------------------------------------------------------------------
+// Static scaling (task page: the DelayedScaling recipe and the calibration step).  The
+// scale is known before the pass - fixed by calibration, or left by the delayed-scaling
+// update - so the cast needs no reduction first: one grid-stride pass casts with it
+// (saturating above 448 * scale).  RECORD: each workgroup also folds the tensor's amax into
+// *acc with one atomicMax on its float bits (non-negative floats, inf and the canonical NaN
+// order as unsigned integers), for the next delayed-scaling update.
+//
+// A fixed scale does not bound the input the way a scale taken from the tensor's own amax
+// does, so the cast differs from the dynamic one in three ways:
+// * x is clamped to +-c, c = RN(448 s), before the division.  Every |x| >= c has a quotient
+//   that encodes to 448 either way (within one float32 ulp of 448 or above it), so the
+//   codes do not change, and the fast quotient keeps |x| <= ~448 s, its precondition: no
+//   overflow of x*r and no infinite input reaches it.
+// * NaN inputs are picked out from their bits and get code 0x7f (the exact encoder's
+//   answer), since the clamp would turn them into numbers.
+// * the fast quotient is used for 2^-80 <= s <= 2^119 only: above 2^119, c overflows to
+//   inf (and past 2^126 the reciprocal 1/s is subnormal and loses bits); below 2^-80 the FMA
+//   residual of a quotient near the smallest code (2^-10) could underflow.  Scales outside the range (and NaN, inf, zero
+//   or negative ones) take the exact path: IEEE division and the software encoder.
+constexpr float kStaticFastMin = 0x1p-80f;
+constexpr float kStaticFastMax = 0x1p119f;
+
+template <int DT>
+__device__ __forceinline__ bool is_nan16(uint32_t h) {
+  return (h & 0x7fffu) > (DT == DT_BF16 ? 0x7f80u : 0x7c00u);
+}
+
+template <int DT>
+__device__ __forceinline__ float quot_static(uint32_t h, float s, float r, float c) {
+  return quot_fast(__builtin_amdgcn_fmed3f(in_to_f32<DT>(h), -c, c), s, r);
+}
+
+// Four 16-bit inputs (two dwords) -> four codes, fast path of the static cast.
+template <int DT>
+__device__ __forceinline__ uint32_t enc4_static(uint32_t w0, uint32_t w1, float s, float r, float c) {
+  const uint32_t h[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
+  uint32_t code = cvt4(quot_static<DT>(h[0], s, r, c), quot_static<DT>(h[1], s, r, c),
+                       quot_static<DT>(h[2], s, r, c), quot_static<DT>(h[3], s, r, c));
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (is_nan16<DT>(h[k])) code = (code & ~(0xffu << (8 * k))) | (0x7fu << (8 * k));
+  return code;
+}
+
+template <int DT>
+__device__ __forceinline__ uint2 enc8_static(const U4& v, float s, float r, float c, bool fast) {
+  if (fast) return make_uint2(enc4_static<DT>(v.x, v.y, s, r, c), enc4_static<DT>(v.z, v.w, s, r, c));
+  return make_uint2(enc4_exact<DT>(v.x, v.y, s), enc4_exact<DT>(v.z, v.w, s));
+}
+
+template <int DT>
+__device__ __forceinline__ uint8_t enc1_static(uint32_t h, float s, float r, float c, bool fast) {
+  if (!fast) return static_cast<uint8_t>(e4m3_encode(in_to_f32<DT>(h) / s));
+  if (is_nan16<DT>(h)) return 0x7fu;
+  const float q = quot_static<DT>(h, s, r, c);
+  return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xff);
+}
+
+template <int DT, bool RECORD>
+__global__ __launch_bounds__(kThreads) void tensor_static_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                 const float* __restrict__ scale_p,
+                                                                 uint8_t* __restrict__ q, uint32_t* acc) {
+  __shared__ uint32_t wave_max[kThreads / 64];
+  const float scale = *scale_p;
+  const bool fast = scale >= kStaticFastMin && scale <= kStaticFastMax;   // false for NaN
+  const float r = 1.0f / scale;
+  const float c = 448.0f * scale;
+  const int64_t nvec = n >> 3;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  uint32_t m = 0;
+  int64_t i = tid;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight per lane
+    U4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = load16(x + ((i + u * stride) << 3));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (RECORD) m = max(m, key8(v[u]));
+      *reinterpret_cast<uint2*>(q + ((i + u * stride) << 3)) = enc8_static<DT>(v[u], scale, r, c, fast);
+    }
+  }
+  for (; i < nvec; i += stride) {
+    const U4 v = load16(x + (i << 3));
+    if constexpr (RECORD) m = max(m, key8(v));
+    *reinterpret_cast<uint2*>(q + (i << 3)) = enc8_static<DT>(v, scale, r, c, fast);
+  }
+  for (int64_t j = (nvec << 3) + tid; j < n; j += stride) {
+    if constexpr (RECORD) m = max(m, x[j] & 0x7fffu);
+    q[j] = enc1_static<DT>(x[j], scale, r, c, fast);
+  }
+  if constexpr (RECORD) {
+    m = max64(m);
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+      atomicMax(acc, __float_as_uint(amax_from_key<DT>(m)));
+    }
+  }
+}
+
+// One delayed-scaling step, one wave.  The amax recorded since the last update (*acc)
+// becomes the ring entry history[step % len], *acc is cleared and the step counted; after
+// every interval-th step *scale = max(history) * 2^margin / 448 (all-zero window -> 1, a NaN
+// in the window -> the canonical NaN).  The ring needs no head pointer: the step count says
+// where the most recent amax is.  Every load is issued up front (step, acc and the whole
+// window in one round trip); the new entry replaces its slot in registers, so no store has
+// to become visible before the maximum is taken, and the stores come last.
+__global__ __launch_bounds__(64) void delayed_update_kernel(float* history, int len, uint32_t* acc,
+                                                            int* step, int interval, int margin,
+                                                            float* scale) {
+  const int lane = threadIdx.x;
+  const int st = *step;
+  const float recorded = __uint_as_float(*acc);
+  const int slot = st % len;
+  float m = 0.0f;
+  bool nan = false;
+  for (int i = lane; i < len; i += 64) {
+    const float h = i == slot ? recorded : history[i];
+    nan |= h != h;
+    m = fmaxf(m, h);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o, 64));
+    nan |= __shfl_xor(static_cast<int>(nan), o, 64) != 0;
+  }
+  if (lane == 0) {
+    history[slot] = recorded;
+    *acc = 0u;
+    *step = st + 1;
+    if ((st + 1) % interval == 0)
+      *scale = nan ? __uint_as_float(kCanonicalNaN)
+                   : (m == 0.0f ? 1.0f : __builtin_amdgcn_ldexpf(m, margin) / 448.0f);
+  }
+}
+
 // Whole-tensor amax, scale and cast in one workgroup, for tensors small enough that one
 // CU streams them in less time than the three-launch path spends on launches (the
 // activations of decode steps).  No atomics and no result word to clear: the workgroup
@@ -499,6 +637,26 @@ void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t*
   uint32_t* w = reinterpret_cast<uint32_t*>(scale);
   if (dt == DT_BF16) tensor_cast_kernel<DT_BF16><<<grid, kThreads, 0, s>>>(xp, n, w, q);
   else tensor_cast_kernel<DT_F16><<<grid, kThreads, 0, s>>>(xp, n, w, q);
+}
+
+void launch_tensor_static(int dt, const void* x, int64_t n, const float* scale, uint8_t* q,
+                          uint32_t* amax_acc, hipStream_t s) {
+  // 8192 elements per workgroup: a quarter of the atomics on the amax word (they serialize
+  // on its one address) for the same loads in flight as the cast kernel
+  const unsigned grid = grid_for(n, kThreads * 8 * 4, kStreamCap);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (dt == DT_BF16) {
+    if (amax_acc) tensor_static_kernel<DT_BF16, true><<<grid, kThreads, 0, s>>>(xp, n, scale, q, amax_acc);
+    else tensor_static_kernel<DT_BF16, false><<<grid, kThreads, 0, s>>>(xp, n, scale, q, nullptr);
+  } else {
+    if (amax_acc) tensor_static_kernel<DT_F16, true><<<grid, kThreads, 0, s>>>(xp, n, scale, q, amax_acc);
+    else tensor_static_kernel<DT_F16, false><<<grid, kThreads, 0, s>>>(xp, n, scale, q, nullptr);
+  }
+}
+
+void launch_delayed_update(float* history, int len, uint32_t* amax_acc, int* step, int interval,
+                           int margin, float* scale, hipStream_t s) {
+  delayed_update_kernel<<<1, 64, 0, s>>>(history, len, amax_acc, step, interval, margin, scale);
 }
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s) {

@@ -171,6 +171,40 @@ fp8_status_t fp8_gemm_scaled_blockwise_ue8m0(const uint8_t* qa, const uint8_t* s
                                              void* c, fp8_dtype_t out_dt, void* stream);
 
 /*
+ * fp8_quantize_static - static scaling (the task page's FP8 recipe and calibration step: a
+ * scale fixed before the pass instead of this tensor's amax): q = e4m3(x / *scale) in one
+ * pass, saturating to +-448 where |x| > 448 * scale.
+ *   scale    : float32 [1] (device), e.g. from calibration or from
+ *              fp8_delayed_scaling_update; finite and > 0 (not checked on the device).
+ *   amax_acc : NULL, or a uint32 (device) that receives max(current, float bits of this
+ *              tensor's amax) by atomic max (float bits of non-negative values, inf and
+ *              the canonical NaN 0x7FC00000 order as integers), for delayed scaling.
+ *   x, q     : as fp8_quantize_per_tensor.
+ * Errors: as fp8_quantize_per_tensor; rows * cols == 0 returns FP8_OK with nothing launched.
+ */
+fp8_status_t fp8_quantize_static(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                 const float* scale, uint8_t* q, uint32_t* amax_acc, void* stream);
+
+/*
+ * fp8_delayed_scaling_update - one step of delayed scaling (the task page's DelayedScaling
+ * recipe: margin, interval), on device-resident state so that it can be captured in a
+ * HIP graph:
+ *   the amax recorded in *amax_acc since the last update is stored in the ring
+ *   history[*step % len] and *amax_acc is cleared; *step is incremented; when the new *step
+ *   is a multiple of `interval`, *scale = max(history) * 2^margin / 448 in float32 (an
+ *   all-zero window gives 1, a NaN in the window gives NaN); otherwise *scale is unchanged.
+ *   history  : float32 [len] (device), the last len amaxes; the most recent is at
+ *              (*step - 1) % len.  Zero-fill it, *amax_acc and *step before the first step.
+ *   amax_acc : uint32 (device), as written by fp8_quantize_static.
+ *   step     : int32 (device), steps so far.
+ *   scale    : float32 [1] (device), the scale fp8_quantize_static uses.
+ * Requires len >= 1, interval >= 1, -126 <= margin <= 126 (else FP8_ERR_BAD_SHAPE); all
+ * pointers non-NULL and 4-byte aligned.  Calls on one state must be ordered (one stream).
+ */
+fp8_status_t fp8_delayed_scaling_update(float* history, int32_t len, uint32_t* amax_acc, int32_t* step,
+                                        int32_t interval, int32_t margin, float* scale, void* stream);
+
+/*
  * fp8_debug_cast_f32 - test hook: q[i] = e4m3(v[i]) with the same device encoder the
  * quantizers use (saturating round to nearest even; NaN -> 0x7F).  v is float32 [n],
  * q is uint8 [n].  n == 0 returns FP8_OK.

@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"fp8_status_string", "fp8_amax", "fp8_quantize_per_tensor",
                           "fp8_quantize_per_token_group", "fp8_gemm_scaled_tensorwise",
                           "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
-                          "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0"}
+                          "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0",
+                          "fp8_quantize_static", "fp8_delayed_scaling_update"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -103,6 +104,23 @@ def test_quantize_validation(L):
     assert d(A16, A16, -1, None) == SHAPE
     assert d(A16, A16, 0, None) == OK
     assert d(None, A16, 8, None) == NULLP
+
+
+def test_static_and_delayed_validation(L):
+    st = L.fp8_quantize_static
+    assert st(A16, 3, 4, 256, A16, A16, None, None) == DTYPE
+    assert st(A16, 0, -1, 256, A16, A16, None, None) == SHAPE
+    assert st(A16, 0, 0, 256, None, None, None, None) == OK             # empty: nothing launched
+    assert st(None, 0, 4, 256, A16, A16, None, None) == NULLP
+    assert st(A16, 0, 4, 256, None, A16, None, None) == NULLP           # scale is required
+    assert st(A16, 0, 4, 256, A16 + 2, A16, None, None) == ALIGN
+    assert st(A16, 0, 4, 256, A16, A16, A16 + 1, None) == ALIGN
+    up = L.fp8_delayed_scaling_update
+    assert up(A16, 0, A16, A16, 4, 0, A16, None) == SHAPE                # empty history
+    assert up(A16, 8, A16, A16, 0, 0, A16, None) == SHAPE                # interval 0
+    assert up(A16, 8, A16, A16, 4, 127, A16, None) == SHAPE              # margin out of range
+    assert up(None, 8, A16, A16, 4, 0, A16, None) == NULLP
+    assert up(A16, 8, A16, A16 + 2, 4, 0, A16, None) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors():
