@@ -125,9 +125,12 @@ def algorithmic_bytes(w, M, scale_fmt="float32", act_scaling="dynamic"):
     gemm = M * K + sa_bytes + N * K + sb_bytes + 2 * M * N
     quant_b = (2 * N * K + N * K + sb_bytes) if w.quantize_b_per_call else 0
     if act_scaling == "delayed":
-        update = 4 + DELAYED_HISTORY * 4 + 4 + 4 + 4 + 4 + 4       # acc rw, history, step rw, scale
-        quant_a += 4 + update
-        quant_b += (4 + update) if w.quantize_b_per_call else 0
+        # beyond the cast (whose scale_used write is sa_bytes): the scale read by the cast, the
+        # amax word (recorded, read, cleared), the history read, one entry written, the step
+        # read and written, the scale read and rewritten
+        update = 4 + 12 + DELAYED_HISTORY * 4 + 4 + 8 + 8
+        quant_a += update
+        quant_b += update if w.quantize_b_per_call else 0
     return quant_a + gemm + quant_b, gemm
 
 
@@ -266,10 +269,10 @@ def main():
     def quantize(s):
         if blockwise:
             quant_groups(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
-        elif delayed:
-            ds_a.quantize(s["a"], q=s["qa"])
+        elif delayed:                       # cast, push the amax, refresh the scale: one launch
+            ds_a.quantize_step(s["a"], q=s["qa"])
             if ds_b is not None:
-                ds_b.quantize(s["b"], q=s["qb"])
+                ds_b.quantize_step(s["b"], q=s["qb"])
         else:
             fp8.fp8_quantize_per_tensor(s["a"], q=s["qa"], scale=s["sa"])
             if w.quantize_b_per_call:
@@ -280,18 +283,14 @@ def main():
             gemm_blockwise = fp8.fp8_gemm_scaled_blockwise_ue8m0 if ue8m0 else fp8.fp8_gemm_scaled_blockwise
             gemm_blockwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
         elif delayed:
-            fp8.fp8_gemm_scaled_tensorwise(s["qa"], ds_a.scale, s["qb"], ds_b.scale if ds_b else s["sb"],
-                                           out=s["c"])
+            fp8.fp8_gemm_scaled_tensorwise(s["qa"], ds_a.scale_used, s["qb"],
+                                           ds_b.scale_used if ds_b else s["sb"], out=s["c"])
         else:
             fp8.fp8_gemm_scaled_tensorwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
 
     def step(s):
         quantize(s)
         gemm(s)
-        if delayed:                         # the scale for the next step
-            ds_a.update()
-            if ds_b is not None:
-                ds_b.update()
 
     # eager warm-up (first launches, lazy initialisation; with delayed scaling at least two
     # intervals, so the scale has reached its steady state), then one eager reference output

@@ -34,6 +34,8 @@ _SIGNATURES = {
     "fp8_gemm_scaled_blockwise_ue8m0": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_quantize_static": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "fp8_delayed_scaling_update": ([_P, _I32, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
+    "fp8_quantize_delayed": ([_P, ctypes.c_int, _I64, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P],
+                             ctypes.c_int),
     "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
 }
 
@@ -263,15 +265,24 @@ def fp8_quantize_static(x, scale, q=None, amax_acc=None):
 
 class DelayedScaling:
     """Device-resident delayed-scaling state: history float32 [len] (a ring), the amax
-    accumulator (int32 storage of the uint32 word), the step count (int32) and the scale
-    (float32 [1], initially `init_scale`)."""
+    accumulator (int32 storage of the uint32 word), the step count (int32), the scale
+    (float32 [1], initially `init_scale`) and the scale the last quantize_step cast with
+    (scale_used)."""
 
     def __init__(self, history_len, interval, margin=0, init_scale=1.0, device="cuda"):
         self.history = torch.zeros(history_len, dtype=torch.float32, device=device)
         self.amax_acc = torch.zeros(1, dtype=torch.int32, device=device)
         self.step = torch.zeros(1, dtype=torch.int32, device=device)
         self.scale = torch.full((1,), float(init_scale), dtype=torch.float32, device=device)
+        self.scale_used = torch.full((1,), float(init_scale), dtype=torch.float32, device=device)
         self.interval, self.margin = int(interval), int(margin)
+
+    def quantize_step(self, x, q=None):
+        """One whole step in one call: cast x with the current scale (copied to
+        scale_used, the scale to hand to the GEMM), push its amax, refresh the scale every
+        interval steps.  Returns q."""
+        return fp8_quantize_delayed(x, self.history, self.amax_acc, self.step, self.interval, self.margin,
+                                    self.scale, self.scale_used, q=q)
 
     def quantize(self, x, q=None):
         """Cast x with the current scale and record its amax."""
@@ -290,6 +301,31 @@ def fp8_delayed_scaling_update(history, amax_acc, step, interval, margin, scale)
                                             ctypes.c_void_p(amax_acc.data_ptr()),
                                             ctypes.c_void_p(step.data_ptr()), interval, margin,
                                             ctypes.c_void_p(scale.data_ptr()), _stream(history)))
+
+
+def fp8_quantize_delayed(x, history, amax_acc, step, interval, margin, scale, scale_used, q=None):
+    """fp8_quantize_static followed by fp8_delayed_scaling_update in one call; the scale
+    the codes were made with is written to scale_used.  Returns q."""
+    x = _as_2d(x)
+    _need_cuda(x, history, amax_acc, step, scale, scale_used)
+    for t, what in ((scale, "scale"), (scale_used, "scale_used")):
+        if t.dtype != torch.float32 or t.numel() != 1:
+            raise TypeError(f"{what} must be one float32 value on the device")
+    for t, what in ((amax_acc, "amax_acc"), (step, "step")):
+        if t.element_size() != 4 or t.numel() != 1:
+            raise TypeError(f"{what} must be one 32-bit word on the device")
+    if history.dtype != torch.float32 or not history.is_contiguous():
+        raise TypeError("history must be a contiguous float32 tensor")
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    _need_cuda(q)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    _check("fp8_quantize_delayed",
+           lib().fp8_quantize_delayed(_ptr(x), _dt(x), R, C, vp(history), history.numel(), vp(amax_acc),
+                                      vp(step), int(interval), int(margin), vp(scale), vp(scale_used),
+                                      _ptr(q), _stream(x)))
+    return q
 
 
 def fp8_debug_cast_f32(v, q=None):

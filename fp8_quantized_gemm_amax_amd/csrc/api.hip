@@ -175,6 +175,26 @@ fp8_status_t fp8_delayed_scaling_update(float* history, int32_t len, uint32_t* a
   return finish_launch();
 }
 
+fp8_status_t fp8_quantize_delayed(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                  float* history, int32_t len, uint32_t* amax_acc, int32_t* step,
+                                  int32_t interval, int32_t margin, float* scale, float* scale_used,
+                                  uint8_t* q, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  if (len < 1 || interval < 1 || margin < -126 || margin > 126) return FP8_ERR_BAD_SHAPE;
+  const int64_t n = rows * cols;
+  if ((n > 0 && (!x || !q)) || !history || !amax_acc || !step || !scale || !scale_used)
+    return FP8_ERR_NULL_POINTER;
+  if ((n > 0 && (!aligned16(x) || !aligned16(q))) || !aligned4(history) || !aligned4(amax_acc) ||
+      !aligned4(step) || !aligned4(scale) || !aligned4(scale_used))
+    return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_delayed_quantize(static_cast<int>(dt), x, n, history, len, amax_acc, step, interval,
+                                   margin, scale, scale_used, q, static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
 fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* stream) {
   if (n < 0) return FP8_ERR_BAD_SHAPE;
   if (n > kMaxElems) return FP8_ERR_TOO_LARGE;

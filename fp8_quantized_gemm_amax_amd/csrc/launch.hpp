@@ -50,6 +50,9 @@ void launch_tensor_static(int dt, const void* x, int64_t n, const float* scale, 
 // One delayed-scaling step on device-resident state (see fp8_delayed_scaling_update).
 void launch_delayed_update(float* history, int len, uint32_t* amax_acc, int* step, int interval,
                            int margin, float* scale, hipStream_t s);
+void launch_delayed_quantize(int dt, const void* x, int64_t n, float* history, int len,
+                             uint32_t* amax_acc, int* step, int interval, int margin, float* scale,
+                             float* scale_used, uint8_t* q, hipStream_t s);
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 

@@ -386,21 +386,18 @@ __device__ __forceinline__ uint8_t enc1_static(uint32_t h, float s, float r, flo
   return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xff);
 }
 
+// The static cast pass of one lane over a grid-strided range (four 16-byte loads in flight):
+// q = e4m3(x / scale) for its elements; returns the lane's largest magnitude key when RECORD.
 template <int DT, bool RECORD>
-__global__ __launch_bounds__(kThreads) void tensor_static_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                                 const float* __restrict__ scale_p,
-                                                                 uint8_t* __restrict__ q, uint32_t* acc) {
-  __shared__ uint32_t wave_max[kThreads / 64];
-  const float scale = *scale_p;
+__device__ __forceinline__ uint32_t static_cast_pass(const uint16_t* __restrict__ x, int64_t n, float scale,
+                                                     uint8_t* __restrict__ q, int64_t tid, int64_t stride) {
   const bool fast = scale >= kStaticFastMin && scale <= kStaticFastMax;   // false for NaN
   const float r = 1.0f / scale;
   const float c = 448.0f * scale;
   const int64_t nvec = n >> 3;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   uint32_t m = 0;
   int64_t i = tid;
-  for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight per lane
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
     U4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = load16(x + ((i + u * stride) << 3));
@@ -419,49 +416,180 @@ __global__ __launch_bounds__(kThreads) void tensor_static_kernel(const uint16_t*
     if constexpr (RECORD) m = max(m, x[j] & 0x7fffu);
     q[j] = enc1_static<DT>(x[j], scale, r, c, fast);
   }
+  return m;
+}
+
+// Largest key over a workgroup of WAVES waves; the result is valid in every lane of wave 0.
+template <int WAVES>
+__device__ __forceinline__ uint32_t block_max_key(uint32_t m, uint32_t* wave_max) {
+  m = max64(m);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t k = 0;
+  if (threadIdx.x < 64) {
+    k = threadIdx.x < WAVES ? wave_max[threadIdx.x] : 0u;
+    k = max64(k);
+  }
+  return k;
+}
+
+template <int DT, bool RECORD>
+__global__ __launch_bounds__(kThreads) void tensor_static_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                 const float* __restrict__ scale_p,
+                                                                 uint8_t* __restrict__ q, uint32_t* acc) {
+  __shared__ uint32_t wave_max[kThreads / 64];
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  const uint32_t m = static_cast_pass<DT, RECORD>(x, n, *scale_p, q, tid, stride);
   if constexpr (RECORD) {
-    m = max64(m);
-    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-      atomicMax(acc, __float_as_uint(amax_from_key<DT>(m)));
-    }
+    const uint32_t k = block_max_key<kThreads / 64>(m, wave_max);
+    if (threadIdx.x == 0) atomicMax(acc, __float_as_uint(amax_from_key<DT>(k)));
   }
 }
 
-// One delayed-scaling step, one wave.  The amax recorded since the last update (*acc)
-// becomes the ring entry history[step % len], *acc is cleared and the step counted; after
-// every interval-th step *scale = max(history) * 2^margin / 448 (all-zero window -> 1, a NaN
+// One delayed-scaling step, carried out by one wave, in two parts.  window_max takes the
+// maximum (and whether a NaN occurs) over the history entries that stay, every slot but
+// st % len, which this step overwrites; push_and_refresh then stores `recorded` (the amax of
+// step st, float bits ordered as integers) in that slot, counts the step and, after every
+// interval-th step, sets *scale = max(window) * 2^margin / 448 (all-zero window -> 1, a NaN
 // in the window -> the canonical NaN).  The ring needs no head pointer: the step count says
-// where the most recent amax is.  Every load is issued up front (step, acc and the whole
-// window in one round trip); the new entry replaces its slot in registers, so no store has
-// to become visible before the maximum is taken, and the stores come last.
+// where the most recent amax is.  Splitting the two lets the window be read before the
+// step's amax is known.
+struct WindowMax {
+  float m;
+  bool nan;
+};
+
+__device__ __forceinline__ WindowMax wave_window_max(WindowMax w) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    w.m = fmaxf(w.m, __shfl_xor(w.m, o, 64));
+    w.nan |= __shfl_xor(static_cast<int>(w.nan), o, 64) != 0;
+  }
+  return w;
+}
+
+// The entry `first` of lane (the history's element lane, when lane < len) may have been
+// loaded ahead of time; the loads do not depend on the slot.
+__device__ __forceinline__ WindowMax window_max(const float* history, int len, int slot, float first) {
+  const int lane = threadIdx.x & 63;
+  WindowMax w{0.0f, false};
+  for (int i = lane; i < len; i += 64) {
+    const float h = i == lane ? first : history[i];
+    if (i == slot) continue;
+    w.nan |= h != h;
+    w.m = fmaxf(w.m, h);
+  }
+  return wave_window_max(w);
+}
+
+__device__ __forceinline__ float history_first(const float* history, int len) {
+  const int lane = threadIdx.x & 63;
+  return lane < len ? history[lane] : 0.0f;
+}
+
+// Lane 0 of the wave stores.
+__device__ __forceinline__ void push_and_refresh(float* history, int len, WindowMax w, float recorded,
+                                                 int st, int* step, int interval, int margin,
+                                                 float* scale) {
+  if ((threadIdx.x & 63) != 0) return;
+  history[st % len] = recorded;
+  *step = st + 1;
+  if ((st + 1) % interval == 0) {
+    const bool nan = w.nan || recorded != recorded;
+    const float m = fmaxf(w.m, recorded);
+    *scale = nan ? __uint_as_float(kCanonicalNaN)
+                 : (m == 0.0f ? 1.0f : __builtin_amdgcn_ldexpf(m, margin) / 448.0f);
+  }
+}
+
+// The update alone: the amax recorded in *acc since the last update is pushed and *acc
+// cleared.  scale_used (may be null) receives the scale before the update: the one the
+// casts since the last update were made with.
 __global__ __launch_bounds__(64) void delayed_update_kernel(float* history, int len, uint32_t* acc,
                                                             int* step, int interval, int margin,
-                                                            float* scale) {
-  const int lane = threadIdx.x;
+                                                            float* scale, float* scale_used) {
   const int st = *step;
   const float recorded = __uint_as_float(*acc);
-  const int slot = st % len;
-  float m = 0.0f;
-  bool nan = false;
-  for (int i = lane; i < len; i += 64) {
-    const float h = i == slot ? recorded : history[i];
-    nan |= h != h;
-    m = fmaxf(m, h);
-  }
-  for (int o = 32; o >= 1; o >>= 1) {
-    m = fmaxf(m, __shfl_xor(m, o, 64));
-    nan |= __shfl_xor(static_cast<int>(nan), o, 64) != 0;
-  }
-  if (lane == 0) {
-    history[slot] = recorded;
+  const float before = *scale;
+  const WindowMax w = window_max(history, len, st % len, history_first(history, len));
+  push_and_refresh(history, len, w, recorded, st, step, interval, margin, scale);
+  if (threadIdx.x == 0) {
     *acc = 0u;
-    *step = st + 1;
-    if ((st + 1) % interval == 0)
-      *scale = nan ? __uint_as_float(kCanonicalNaN)
-                   : (m == 0.0f ? 1.0f : __builtin_amdgcn_ldexpf(m, margin) / 448.0f);
+    if (scale_used) *scale_used = before;
+  }
+}
+
+// Static cast + update in one launch, for tensors of up to kSmallTensor elements: one
+// workgroup casts with *scale, reduces the tensor's amax in LDS (folding in whatever *acc
+// holds), and its first wave then does the update.  Every wave has read *scale before the
+// barrier that precedes the update, so the scale may be rewritten.  No atomics.  (Larger
+// tensors take the static cast and the update as two launches: with many workgroups the
+// update could only start once all of them have recorded their amax, which inside one
+// launch takes a device-scope release per workgroup - an L2 write-back on this chip - and
+// that costs more than the second launch.)
+constexpr int kSmallThreads = 1024;
+constexpr int64_t kSmallTensor = int64_t{1} << 15;   // whole-tensor paths in one workgroup up to here
+
+// The static cast of a tensor of at most kSmallTensor elements by one workgroup of
+// kSmallThreads: each thread's (at most four) 16-byte pieces and tail element are loaded
+// before the scale is needed, so the scale's load overlaps theirs instead of preceding them.
+// Returns the thread's largest magnitude key; *scale_out receives the scale.
+template <int DT>
+__device__ __forceinline__ uint32_t static_cast_small(const uint16_t* __restrict__ x, int64_t n,
+                                                      const float* scale_p, float* scale_out,
+                                                      uint8_t* __restrict__ q) {
+  static_assert(kSmallTensor == int64_t{4} * 8 * kSmallThreads, "four pieces per thread");
+  const float scale = *scale_p;                     // issued first; waited for after x's loads
+  const int t = threadIdx.x;
+  const int64_t nvec = n >> 3;
+  // x as a range-checked buffer of 2n bytes: loads past it read zeros, so every load is
+  // issued unconditionally (no branch, no wait between them)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), static_cast<short>(0), static_cast<int>(2 * n), static_cast<int>(0x00020000));
+  U4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    v[u] = __builtin_bit_cast(U4, __builtin_amdgcn_raw_buffer_load_b128(xr, 16 * (t + u * kSmallThreads), 0, 0));
+  const int64_t j = (nvec << 3) + t;                // n - 8 * nvec < 8 tail elements
+  const uint32_t tail = __builtin_amdgcn_raw_buffer_load_b16(xr, static_cast<int>(2 * j), 0, 0);
+  const bool fast = scale >= kStaticFastMin && scale <= kStaticFastMax;
+  const float r = 1.0f / scale;
+  const float c = 448.0f * scale;
+  // the keys are selected, not branched on, so that no load is sunk past the scale's
+  uint32_t m = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) m = max(m, t + u * kSmallThreads < nvec ? key8(v[u]) : 0u);
+  m = max(m, j < n ? (tail & 0x7fffu) : 0u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = t + u * kSmallThreads;
+    if (i < nvec) *reinterpret_cast<uint2*>(q + (i << 3)) = enc8_static<DT>(v[u], scale, r, c, fast);
+  }
+  if (j < n) q[j] = enc1_static<DT>(tail, scale, r, c, fast);
+  *scale_out = scale;
+  return m;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kSmallThreads) void delayed_small_kernel(
+    const uint16_t* __restrict__ x, int64_t n, float* history, int len, uint32_t* acc, int* step,
+    int interval, int margin, float* scale, float* scale_used, uint8_t* __restrict__ q) {
+  __shared__ uint32_t wave_max[kSmallThreads / 64];
+  // the state the update reads is loaded with x, not after the cast: nothing writes it
+  // before the update
+  const int st = *step;
+  const uint32_t acc0 = *acc;
+  const float first = history_first(history, len);
+  float s;
+  const uint32_t m = static_cast_small<DT>(x, n, scale, &s, q);
+  const uint32_t k = block_max_key<kSmallThreads / 64>(m, wave_max);
+  if (threadIdx.x >= 64) return;
+  const uint32_t recorded = max(acc0, __float_as_uint(amax_from_key<DT>(k)));
+  const WindowMax w = window_max(history, len, st % len, first);
+  push_and_refresh(history, len, w, __uint_as_float(recorded), st, step, interval, margin, scale);
+  if (threadIdx.x == 0) {
+    *acc = 0u;
+    *scale_used = s;
   }
 }
 
@@ -470,8 +598,6 @@ __global__ __launch_bounds__(64) void delayed_update_kernel(float* history, int 
 // activations of decode steps).  No atomics and no result word to clear: the workgroup
 // reduces in LDS, writes the finished float, and casts from the same scale.  The second
 // pass re-reads x, which the first pass has just brought into the caches.
-constexpr int kSmallThreads = 1024;
-
 template <int DT, bool WANT_SCALE, bool WRITE_Q>
 __global__ __launch_bounds__(kSmallThreads) void tensor_small_kernel(const uint16_t* __restrict__ x,
                                                                      int64_t n, uint32_t* word,
@@ -527,7 +653,6 @@ inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
 }
 
 constexpr int64_t kStreamCap = 256 * 16;     // 16 workgroups per CU on 256 CUs
-constexpr int64_t kSmallTensor = int64_t{1} << 15;   // whole-tensor path in one workgroup up to here
 constexpr int64_t kReduceCap = 256 * 4;      // whole-tensor reduction workgroups
 constexpr int64_t kGroupCap = 256 * 256;     // group/block kernels loop beyond this grid
 
@@ -656,7 +781,24 @@ void launch_tensor_static(int dt, const void* x, int64_t n, const float* scale, 
 
 void launch_delayed_update(float* history, int len, uint32_t* amax_acc, int* step, int interval,
                            int margin, float* scale, hipStream_t s) {
-  delayed_update_kernel<<<1, 64, 0, s>>>(history, len, amax_acc, step, interval, margin, scale);
+  delayed_update_kernel<<<1, 64, 0, s>>>(history, len, amax_acc, step, interval, margin, scale, nullptr);
+}
+
+void launch_delayed_quantize(int dt, const void* x, int64_t n, float* history, int len,
+                             uint32_t* amax_acc, int* step, int interval, int margin, float* scale,
+                             float* scale_used, uint8_t* q, hipStream_t s) {
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (n <= kSmallTensor) {
+    if (dt == DT_BF16)
+      delayed_small_kernel<DT_BF16><<<1, kSmallThreads, 0, s>>>(xp, n, history, len, amax_acc, step,
+                                                               interval, margin, scale, scale_used, q);
+    else
+      delayed_small_kernel<DT_F16><<<1, kSmallThreads, 0, s>>>(xp, n, history, len, amax_acc, step,
+                                                              interval, margin, scale, scale_used, q);
+    return;
+  }
+  launch_tensor_static(dt, x, n, scale, q, amax_acc, s);
+  delayed_update_kernel<<<1, 64, 0, s>>>(history, len, amax_acc, step, interval, margin, scale, scale_used);
 }
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s) {

@@ -205,6 +205,26 @@ fp8_status_t fp8_delayed_scaling_update(float* history, int32_t len, uint32_t* a
                                         int32_t interval, int32_t margin, float* scale, void* stream);
 
 /*
+ * fp8_quantize_delayed - one delayed-scaling step of one tensor in one call (the task
+ * page's DelayedScaling recipe): exactly fp8_quantize_static(x, scale, q, amax_acc)
+ * followed by fp8_delayed_scaling_update(history, len, amax_acc, step, interval, margin,
+ * scale), and in addition
+ *   scale_used : float32 [1] (device) output, the scale q was made with (the value *scale
+ *                had on entry): the one the GEMM that consumes q must apply, since *scale
+ *                may already hold the next step's scale when the call returns.
+ * One launch for up to 32768 elements, two (the cast, then the update) above.
+ * history, amax_acc, step, scale, interval, margin: as fp8_delayed_scaling_update (amax_acc
+ * may hold amaxes recorded by fp8_quantize_static since the last update; they are folded
+ * in).  x, q: as fp8_quantize_per_tensor; rows * cols == 0 is allowed (x and q may then be
+ * NULL) and still performs the update with this tensor's amax taken as 0.
+ * Errors: those of the two calls it replaces.  Calls on one state must be ordered.
+ */
+fp8_status_t fp8_quantize_delayed(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
+                                  float* history, int32_t len, uint32_t* amax_acc, int32_t* step,
+                                  int32_t interval, int32_t margin, float* scale, float* scale_used,
+                                  uint8_t* q, void* stream);
+
+/*
  * fp8_debug_cast_f32 - test hook: q[i] = e4m3(v[i]) with the same device encoder the
  * quantizers use (saturating round to nearest even; NaN -> 0x7F).  v is float32 [n],
  * q is uint8 [n].  n == 0 returns FP8_OK.

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
                           "fp8_quantize_per_token_group", "fp8_gemm_scaled_tensorwise",
                           "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
                           "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0",
-                          "fp8_quantize_static", "fp8_delayed_scaling_update"}
+                          "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -121,6 +121,31 @@ def test_static_and_delayed_validation(L):
     assert up(A16, 8, A16, A16, 4, 127, A16, None) == SHAPE              # margin out of range
     assert up(None, 8, A16, A16, 4, 0, A16, None) == NULLP
     assert up(A16, 8, A16, A16 + 2, 4, 0, A16, None) == ALIGN
+
+
+def test_fused_delayed_validation(L):
+    """fp8_quantize_delayed(x, dt, rows, cols, history, len, acc, step, interval, margin,
+    scale, scale_used, q, stream): only failing cases (an empty tensor still launches the
+    update)."""
+    fq = L.fp8_quantize_delayed
+
+    def call(x=A16, dt=0, rows=4, cols=256, hist=A16, n=8, acc=A16, step=A16, interval=4, margin=0,
+             scale=A16, used=A16, q=A16):
+        return fq(x, dt, rows, cols, hist, n, acc, step, interval, margin, scale, used, q, None)
+
+    assert call(dt=5) == DTYPE
+    assert call(rows=-1) == SHAPE
+    assert call(n=0) == SHAPE
+    assert call(interval=0) == SHAPE
+    assert call(margin=-127) == SHAPE
+    assert call(x=None) == NULLP
+    assert call(q=None) == NULLP
+    assert call(rows=0, hist=None) == NULLP                             # state is needed even when empty
+    assert call(step=None) == NULLP
+    assert call(used=None) == NULLP
+    assert call(x=A16 + 4) == ALIGN
+    assert call(step=A16 + 2) == ALIGN
+    assert call(rows=0, x=MIS, q=MIS, used=A16 + 1) == ALIGN             # x, q unused when empty
 
 
 def test_binding_refuses_cpu_tensors():

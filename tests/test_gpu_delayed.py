@@ -9,7 +9,8 @@ import torch
 import oracle
 import fp8_quantized_gemm_amax_amd as fp8
 from fp8_quantized_gemm_amax_amd import workloads as wl
-from parity_util import DEV, to_dev, guarded_u8, guard_intact, host_u8, assert_bytes_equal
+from parity_util import (DEV, to_dev, u8_to_dev, f32_to_dev, guarded_u8, guard_intact, host_u8,
+                         out_to_f64, assert_bytes_equal)
 
 pytestmark = pytest.mark.gpu
 
@@ -182,3 +183,99 @@ def test_delayed_step_captured_in_a_graph():
             h, step, scale = oracle.delayed_step(h, step, scale, amax, 2, 0)
         assert_bytes_equal(host_u8(q), q_want, f"replay {rep} last codes")
         check_state(ds, h, step, scale, f"replay {rep}")
+
+
+# ---- the whole step in one call (fp8_quantize_delayed) ----
+
+def check_fused_state(ds, h_want, step_want, scale_want, used_want, label):
+    check_state(ds, h_want, step_want, scale_want, label)
+    assert canonical_bits(float(ds.scale_used.cpu()[0])) == canonical_bits(used_want), label
+
+
+@pytest.mark.parametrize("shape", [(33, 640), (64, 512), (257, 509), (1000, 1001), (3, 8191)])
+@pytest.mark.parametrize("length,interval,margin", [(3, 4, 0), (5, 1, 1), (70, 3, -1)])
+def test_fused_sequence_matches_oracle(shape, length, interval, margin):
+    """Up to 32768 elements: one launch, one workgroup; above: the static cast and the
+    update.  Every step's codes and scale_used against the oracle's static cast with the
+    scale before the step, then the state after it."""
+    rng = np.random.default_rng(shape[0] + 7 * length)
+    ds = fp8.DelayedScaling(length, interval, margin, init_scale=0.25, device=DEV)
+    h, step, scale = np.zeros(length, np.float32), 0, np.float32(0.25)
+    for k in range(10):
+        bits = wl.to_bf16_bits(rng.standard_t(4, shape) * 2.0 ** rng.integers(-5, 9))
+        q = ds.quantize_step(to_dev(bits))
+        q_want, amax = oracle.quantize_static(bits, "bf16", scale)
+        assert_bytes_equal(host_u8(q), q_want, f"{shape} step {k} codes")
+        used = scale
+        h, step, scale = oracle.delayed_step(h, step, scale, amax, interval, margin)
+        check_fused_state(ds, h, step, scale, used, f"{shape} step {k}")
+
+
+@pytest.mark.parametrize("shape", [(16, 128), (512, 2048)])
+def test_fused_folds_in_recorded_amax_and_empty_tensors(shape):
+    """Amaxes recorded by fp8_quantize_static since the last update are folded into the
+    fused call's push; an empty tensor pushes what was recorded (0 when nothing was)."""
+    rng = np.random.default_rng(3)
+    ds = fp8.DelayedScaling(4, 1, 0, init_scale=1.0, device=DEV)
+    big = wl.to_bf16_bits(rng.standard_normal(shape) * 300.0)
+    small = wl.to_bf16_bits(rng.standard_normal(shape))
+    fp8.fp8_quantize_static(to_dev(big), ds.scale, amax_acc=ds.amax_acc)
+    ds.quantize_step(to_dev(small))
+    h, step, scale = np.zeros(4, np.float32), 0, np.float32(1.0)
+    amax = max(oracle.quantize_static(big, "bf16", scale)[1], oracle.quantize_static(small, "bf16", scale)[1])
+    h, step, scale = oracle.delayed_step(h, step, scale, amax, 1, 0)
+    check_fused_state(ds, h, step, scale, np.float32(1.0), "folded")
+    empty = torch.empty((0, shape[1]), dtype=torch.bfloat16, device=DEV)
+    used = scale
+    ds.quantize_step(empty)
+    h, step, scale = oracle.delayed_step(h, step, scale, np.float32(0), 1, 0)
+    check_fused_state(ds, h, step, scale, used, "empty tensor")
+
+
+def test_fused_step_captured_in_a_graph():
+    """One graph holding fused steps on a one-workgroup tensor and (twice) a many-workgroup
+    tensor, and a tensorwise GEMM fed by scale_used, replayed several times with eager work
+    between the replays; every replay against the oracle's sequence."""
+    rng = np.random.default_rng(11)
+    shapes = [(16, 1024), (512, 2048), (512, 2048)]
+    xs = [wl.to_bf16_bits(rng.standard_normal(s) * 2.0 ** e) for s, e in zip(shapes, (0, 4, -3))]
+    xdev = [to_dev(b) for b in xs]
+    ds_small = fp8.DelayedScaling(3, 2, 0, init_scale=1.0, device=DEV)
+    ds_big = fp8.DelayedScaling(3, 2, 0, init_scale=1.0, device=DEV)
+    qs = [torch.empty(s, dtype=torch.uint8, device=DEV) for s in shapes]
+    w_bits = wl.to_bf16_bits(rng.standard_normal((256, 2048)) * 0.02)
+    qw_h, sw_h = oracle.quantize_per_tensor(w_bits, "bf16")
+    qw, sw = u8_to_dev(qw_h), f32_to_dev(sw_h)
+    c = torch.empty((512, 256), dtype=torch.bfloat16, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            ds_small.quantize_step(xdev[0], q=qs[0])
+            ds_big.quantize_step(xdev[1], q=qs[1])
+            ds_big.quantize_step(xdev[2], q=qs[2])
+            fp8.fp8_gemm_scaled_tensorwise(qs[2], ds_big.scale_used, qw, sw, out=c)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    check_fused_state(ds_big, np.zeros(3, np.float32), 0, np.float32(1.0), np.float32(1.0), "after capture")
+    st_s = (np.zeros(3, np.float32), 0, np.float32(1.0))
+    st_b = (np.zeros(3, np.float32), 0, np.float32(1.0))
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.ones(1024, device=DEV).sum().item() == 1024.0      # eager work between replays
+        used_s = st_s[2]
+        q0, a0 = oracle.quantize_static(xs[0], "bf16", used_s)
+        st_s = oracle.delayed_step(*st_s, a0, 2, 0)
+        assert_bytes_equal(host_u8(qs[0]), q0, f"replay {rep} small codes")
+        check_fused_state(ds_small, *st_s, used_s, f"replay {rep} small")
+        for i in (1, 2):
+            used_b = st_b[2]
+            qi, ai = oracle.quantize_static(xs[i], "bf16", used_b)
+            st_b = oracle.delayed_step(*st_b, ai, 2, 0)
+            assert_bytes_equal(host_u8(qs[i]), qi, f"replay {rep} big codes {i}")
+        check_fused_state(ds_big, *st_b, used_b, f"replay {rep} big")
+        r = oracle.check_gemm(out_to_f64(c), oracle.gemm_tensorwise_ref(qi, used_b, qw_h, sw_h),
+                              oracle.bound_tensorwise(qi, used_b, qw_h, sw_h), "bf16")
+        assert r["ok"], f"replay {rep} GEMM: {r}"
