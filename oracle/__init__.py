@@ -27,6 +27,11 @@ It is a plain, slow, obviously correct restatement of what the pages define:
   with the decoded scales.  Source: "FP8 chi tiết", section on the UE8M0 scale
   format.
 
+* ``rowwise`` - per-channel scaling: one scale per row (per output channel of the
+  weights, per token of the activations), the cast with it, and the product with
+  sa[m] * sb[n].  Source: the Transformer Engine page §5 (per-channel scaling of the
+  weights) with §3 steps 2-6.
+
 * ``delayed`` - static scaling (a scale fixed in advance; saturation) and the
   delayed-scaling amax history (max over the window, times 2^margin, every
   `interval` steps).  Source: the task page's DelayedScaling recipe and calibration
@@ -51,6 +56,7 @@ from .gemm import (gemm_tensorwise_ref, gemm_blockwise_ref, bound_tensorwise,
 from .ue8m0 import (e8m0_decode, e8m0_from_amax, quantize_groups_ue8m0,
                     gemm_blockwise_ue8m0_ref, bound_blockwise_ue8m0)
 from .delayed import quantize_static, delayed_scale_from_history, delayed_step
+from .rowwise import amax_rows, quantize_rowwise, gemm_rowwise_ref, bound_rowwise
 
 __all__ = [
     "E4M3_MAX", "decode_e4m3", "positive_values", "encode_e4m3", "nonneg_breakpoints",
@@ -60,4 +66,5 @@ __all__ = [
     "output_ulp", "check_gemm",
     "e8m0_decode", "e8m0_from_amax", "quantize_groups_ue8m0", "gemm_blockwise_ue8m0_ref",
     "bound_blockwise_ue8m0", "quantize_static", "delayed_scale_from_history", "delayed_step",
+    "amax_rows", "quantize_rowwise", "gemm_rowwise_ref", "bound_rowwise",
 ]
