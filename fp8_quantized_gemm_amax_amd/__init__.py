@@ -9,12 +9,12 @@ from .binding import (Fp8Error, fp8_amax, fp8_quantize_per_tensor, fp8_quantize_
                       fp8_gemm_scaled_tensorwise, fp8_gemm_scaled_blockwise, fp8_debug_cast_f32,
                       fp8_quantize_per_token_group_ue8m0, fp8_gemm_scaled_blockwise_ue8m0,
                       e8m0_row_bytes, fp8_quantize_static, fp8_delayed_scaling_update, fp8_quantize_delayed,
-                      DelayedScaling,
+                      DelayedScaling, fp8_quantize_rowwise, fp8_gemm_scaled_rowwise,
                       lib, LIB_PATH)
 
 __all__ = ["Fp8Error", "fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_per_token_group",
            "fp8_gemm_scaled_tensorwise", "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
            "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0", "e8m0_row_bytes",
            "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
-           "DelayedScaling",
+           "DelayedScaling", "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise",
            "lib", "LIB_PATH"]

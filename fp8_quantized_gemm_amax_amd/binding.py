@@ -32,6 +32,8 @@ _SIGNATURES = {
     "fp8_gemm_scaled_blockwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_quantize_per_token_group_ue8m0": ([_P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "fp8_gemm_scaled_blockwise_ue8m0": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "fp8_quantize_rowwise": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_gemm_scaled_rowwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_quantize_static": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "fp8_delayed_scaling_update": ([_P, _I32, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "fp8_quantize_delayed": ([_P, ctypes.c_int, _I64, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P],
@@ -164,6 +166,24 @@ def fp8_quantize_per_token_group(x, group_rows=1, group_cols=128, q=None, scales
     return q, scales
 
 
+def fp8_quantize_rowwise(x, q=None, scales=None):
+    """One scale per row (a token of the activations, an output channel of the weights).
+    Returns (q uint8 [R, C], scales float32 [R])."""
+    x = _as_2d(x)
+    _need_cuda(x)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R,), dtype=torch.float32, device=x.device)
+    _need_cuda(q, scales)
+    if scales.numel() != R:
+        raise ValueError(f"rowwise scales must have {R} entries, got {scales.numel()}")
+    _check("fp8_quantize_rowwise",
+           lib().fp8_quantize_rowwise(_ptr(x), _dt(x), R, C, _ptr(q), _ptr(scales), _stream(x)))
+    return q, scales
+
+
 def e8m0_row_bytes(groups):
     """Bytes per row of a UE8M0 scale tensor with `groups` scales (four per 32-bit word)."""
     return (groups + 3) // 4 * 4
@@ -213,6 +233,15 @@ def fp8_gemm_scaled_tensorwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=Non
     if sa.numel() != 1 or sb.numel() != 1:
         raise ValueError("tensorwise scales are single float32 values")
     return _gemm("fp8_gemm_scaled_tensorwise", qa, sa, qb, sb, out_dtype, out)
+
+
+def fp8_gemm_scaled_rowwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
+    """C [M, N] = (qa @ qb^T) * sa[m] * sb[n]; sa float32 [M] (per token), sb float32 [N]
+    (per output channel)."""
+    M, N = qa.shape[0], qb.shape[0]
+    if sa.numel() != M or sb.numel() != N:
+        raise ValueError(f"rowwise scales must have {M} and {N} entries, got {sa.numel()} and {sb.numel()}")
+    return _gemm("fp8_gemm_scaled_rowwise", qa, sa, qb, sb, out_dtype, out)
 
 
 def fp8_gemm_scaled_blockwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):

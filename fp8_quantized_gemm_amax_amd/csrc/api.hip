@@ -32,7 +32,7 @@ fp8_status_t finish_launch() {
 fp8_status_t gemm_common(int mode, const uint8_t* qa, const void* sa, const uint8_t* qb,
                          const void* sb, int64_t M, int64_t N, int64_t K, void* c,
                          fp8_dtype_t out_dt, void* stream) {
-  const bool blockwise = mode != fp8amax::SM_TENSOR;
+  const bool blockwise = fp8amax::slab_scaled(mode);
   if (M < 0 || N < 0 || K <= 0) return FP8_ERR_BAD_SHAPE;
   if (blockwise ? (K % 128 != 0) : (K % 16 != 0)) return FP8_ERR_BAD_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8_ERR_TOO_LARGE;
@@ -95,6 +95,25 @@ fp8_status_t fp8_quantize_per_tensor(const void* x, fp8_dtype_t dt, int64_t rows
   (void)hipGetLastError();
   fp8amax::launch_tensor_quantize(static_cast<int>(dt), x, n, scale, q, s);
   return finish_launch();
+}
+
+fp8_status_t fp8_quantize_rowwise(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols, uint8_t* q,
+                                  float* scales, void* stream) {
+  fp8_status_t st = check_2d(rows, cols);
+  if (st != FP8_OK) return st;
+  if (!valid_dt(dt)) return FP8_ERR_BAD_DTYPE;
+  if (rows == 0) return FP8_OK;
+  if (!scales || (cols > 0 && (!x || !q))) return FP8_ERR_NULL_POINTER;
+  if ((x && !aligned16(x)) || (q && !aligned16(q)) || !aligned4(scales)) return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_rows(static_cast<int>(dt), x, rows, cols, q, scales, static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+fp8_status_t fp8_gemm_scaled_rowwise(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                     const float* sb, int64_t M, int64_t N, int64_t K, void* c,
+                                     fp8_dtype_t out_dt, void* stream) {
+  return gemm_common(fp8amax::SM_ROW, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
 }
 
 fp8_status_t fp8_quantize_per_token_group(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,

@@ -8,9 +8,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace fp8amax {
 
 enum : int { DT_BF16 = 0, DT_F16 = 1 };
+
+// The factor a GEMM epilogue multiplies the float32 accumulator of C[m, n] by: `alpha`
+// = sa * sb with one scale per tensor; sa[m] * sb[n] with one scale per row of A (token)
+// and of B (output channel; the Transformer Engine page's per-channel scaling); `alpha`
+// = 1 in the slab-scaled modes, whose scales were applied inside the K loop.
+template <int SM>
+__device__ __forceinline__ float out_factor(float alpha, const float* sa, const float* sb, int m, int n) {
+  if constexpr (SM == SM_ROW) return sa[m] * sb[n];
+  else return alpha;
+}
 
 // Exact float32 value of a 16-bit input pattern (low 16 bits of `h`).
 template <int DT>

@@ -6,7 +6,9 @@
 //     Engine page "Что такое FP8 инференс на H100 (Transformer Engine)?", section 3 steps
 //     5-6 and the pseudocode);
 //   blockwise: each 128-wide K slab g has its own sa[m, g] * sb[n / 128, g] ("FP8 chi
-//     tiết", opening bullets), applied in registers to that slab's float32 partial sum.
+//     tiết", opening bullets), applied in registers to that slab's float32 partial sum;
+//   rowwise: scale = sa[m] * sb[n], one scale per token and per output channel (the
+//     Transformer Engine page §5, per-channel scaling), applied once like tensorwise.
 //
 // Design (CDNA4): a workgroup of 4 waves computes a BM x BN tile.  Each K step is one
 // 128-byte slab: the A and B slabs are staged global -> VGPR -> LDS with a double buffer
@@ -77,7 +79,7 @@ template <int BM, int BN, int WM, int WN, int SM, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m) {
-  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
   const float* __restrict__ sb = static_cast<const float*>(sb_);
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   }
 
   float alpha = 1.0f;
-  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
   const bool vec_store = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       const int n = wave_n0 + 16 * j + 4 * kq;
       uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * alpha);
+      for (int r = 0; r < 4; ++r)
+        h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
       if (vec_store && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
@@ -318,7 +321,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m,
     int tiles_n) {
-  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
   const float* __restrict__ sb = static_cast<const float*>(sb_);
@@ -467,7 +470,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   }
 
   float alpha = 1.0f;
-  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
   const bool vec_store = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -479,7 +482,8 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
       const int n = wave_n0 + 16 * j + 4 * kq;
       uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * alpha);
+      for (int r = 0; r < 4; ++r)
+        h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
       if (vec_store && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
@@ -511,7 +515,7 @@ template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
 __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, int cw, uint16_t* __restrict__ c) {
-  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
   const float* __restrict__ sb = static_cast<const float*>(sb_);
@@ -672,7 +676,7 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
   }
 
   float alpha = 1.0f;
-  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
   const bool vec_store = (N & 3) == 0;
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
@@ -684,7 +688,8 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
       const int n = n0 + 16 * j + 4 * kq;
       uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * alpha);
+      for (int r = 0; r < 4; ++r)
+        h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
       if (vec_store && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
@@ -725,7 +730,7 @@ void launch_cfg(const uint8_t* qa, const void* sa, const uint8_t* qb, const void
 template <int SM, int OUT>
 void launch_gemm_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
-  constexpr bool BW = SM != SM_TENSOR;
+  constexpr bool BW = slab_scaled(SM);
   if (gemv_fits(M, K)) {
     launch_gemv(SM, OUT, qa, sa, qb, sb, M, N, K, c, s);
     return;
@@ -771,7 +776,8 @@ void launch_gemm_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t*
 
 void launch_gemm(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
                  const void* sb, int M, int N, int K, void* c, hipStream_t s) {
-  if (mode == SM_E8M0) launch_gemm_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  if (mode == SM_ROW) launch_gemm_m<SM_ROW>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  else if (mode == SM_E8M0) launch_gemm_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
   else if (mode == SM_BLOCK) launch_gemm_m<SM_BLOCK>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
   else launch_gemm_m<SM_TENSOR>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
 }

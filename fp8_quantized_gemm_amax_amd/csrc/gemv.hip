@@ -68,7 +68,7 @@ template <int SM, int OUT, int WAVES, int UNROLL, int NB, int MB>
 __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c) {
-  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
   const float* __restrict__ sb = static_cast<const float*>(sb_);
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
         }
   }
   float alpha = 1.0f;
-  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
     const int m = 16 * b + r16;
@@ -224,7 +224,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
       const int n = n0 + 16 * j + 4 * kq;
       uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * alpha);
+      for (int r = 0; r < 4; ++r)
+        h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
       if ((N & 3) == 0 && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
@@ -250,7 +251,7 @@ template <int SM, int OUT, int MT, int RPW, int UNROLL>
 __global__ __launch_bounds__(256) void gemv_valu_kernel(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c) {
-  constexpr bool BLOCKWISE = SM != SM_TENSOR;
+  constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
   const float* __restrict__ sb = static_cast<const float*>(sb_);
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
       for (int o = 32; o >= 1; o >>= 1) acc[m][r] += __shfl_xor(acc[m][r], o, 64);
 
   float alpha = 1.0f;
-  if constexpr (!BLOCKWISE) alpha = sa[0] * sb[0];
+  if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
   // lane m * RPW + r writes C[m, row0 + r]
   float mine = 0.0f;
 #pragma unroll
@@ -392,7 +393,8 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
       if (lane == m * RPW + r) mine = acc[m][r];
   const int m = lane / RPW, r = lane % RPW;
   if (lane < MT * RPW && m < M && r < rows)
-    c[static_cast<int64_t>(m) * N + row0 + r] = static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * alpha));
+    c[static_cast<int64_t>(m) * N + row0 + r] =
+        static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * out_factor<SM>(alpha, sa, sb, m, row0 + r)));
 }
 
 template <int BW, int OUT, int MT, int RPW, int UNROLL>
@@ -436,7 +438,8 @@ bool gemv_fits(int M, int K) {
 
 void launch_gemv(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
                  const void* sb, int M, int N, int K, void* c, hipStream_t s) {
-  if (mode == SM_E8M0) launch_gemv_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  if (mode == SM_ROW) launch_gemv_m<SM_ROW>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  else if (mode == SM_E8M0) launch_gemv_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
   else if (mode == SM_BLOCK) launch_gemv_m<SM_BLOCK>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
   else launch_gemv_m<SM_TENSOR>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
 }

@@ -10,8 +10,13 @@ namespace fp8amax {
 //   SM_TENSOR: one float32 scale per operand;
 //   SM_BLOCK:  float32 scales per 1x128 activation group and 128x128 weight block;
 //   SM_E8M0:   the same groups and blocks with UE8M0 scales, one e8m0fnu byte each,
-//              every scale row padded to whole 32-bit words (e8m0_row_bytes).
-enum ScaleMode { SM_TENSOR = 0, SM_BLOCK = 1, SM_E8M0 = 2 };
+//              every scale row padded to whole 32-bit words (e8m0_row_bytes);
+//   SM_ROW:    one float32 scale per row of A (token) and per row of B (output channel).
+enum ScaleMode { SM_TENSOR = 0, SM_BLOCK = 1, SM_E8M0 = 2, SM_ROW = 3 };
+
+// Modes whose scales change every 128-wide K slab, applied inside the K loop; the others
+// scale the finished float32 accumulator once in the epilogue.
+__host__ __device__ constexpr bool slab_scaled(int sm) { return sm == SM_BLOCK || sm == SM_E8M0; }
 
 // Bytes per row of a UE8M0 scale tensor with `groups` scales: four per 32-bit word.
 __host__ __device__ constexpr int64_t e8m0_row_bytes(int64_t groups) { return (groups + 3) & ~int64_t{3}; }
@@ -25,6 +30,10 @@ void launch_groups(int dt, const void* x, int64_t rows, int64_t cols, int32_t gr
 // in rows of e8m0_row_bytes(groups per row) bytes whose padding is set to 127.
 void launch_groups_e8m0(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
                         uint8_t* q, uint8_t* codes, hipStream_t s);
+
+// One float32 scale per row: amax of the row / 448, the row cast with it.
+void launch_rows(int dt, const void* x, int64_t rows, int64_t cols, uint8_t* q, float* scales,
+                 hipStream_t s);
 
 // Whole-tensor amax of n elements into the word `word`.  want_scale = false: the word ends
 // as the float amax.  want_scale = true: the word holds a pending reduction key that

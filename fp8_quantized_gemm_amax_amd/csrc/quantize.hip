@@ -190,6 +190,101 @@ __global__ __launch_bounds__(kThreads) void group_1x128_scalar_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// Per-row scales (per output channel of the weights, per token of the activations; the
+// Transformer Engine page's per-channel scaling): scale = amax of the row / 448, the row
+// cast with it.  Rows of up to 16384 elements stay in registers between the reduction and
+// the cast: WPR = 1 gives a row to one wave (VEC 16-byte pieces per lane, up to 4096
+// elements), WPR = 4 to the whole workgroup (up to 16384).  Each row is read through a
+// buffer resource of exactly its bytes, so pieces past its end load as zeros and every load
+// is issued without a branch.  cols % 8 == 0 (every row starts 16-byte aligned).
+template <int DT, int WPR, int VEC>
+__global__ __launch_bounds__(kThreads) void rows_vec_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scales) {
+  static_assert(WPR == 1 || WPR == kThreads / 64, "a row per wave or per workgroup");
+  constexpr int T = 64 * WPR;                  // threads per row
+  constexpr int RPB = kThreads / T;            // rows per workgroup and pass
+  __shared__ uint32_t part[kThreads / 64];
+  const int lt = threadIdx.x % T;
+  const int grp = threadIdx.x / T;
+  const int64_t nv = cols >> 3;
+  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * RPB; row0 < rows;
+       row0 += static_cast<int64_t>(gridDim.x) * RPB) {
+    // the row is uniform over its wave(s): keep it, and the resource, in scalar registers
+    const int64_t row = row0 + __builtin_amdgcn_readfirstlane(grp);
+    const bool live = row < rows;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x + (live ? row : 0) * cols), static_cast<short>(0),
+        live ? static_cast<int>(2 * cols) : 0, static_cast<int>(0x00020000));
+    U4 v[VEC];
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      v[u] = __builtin_bit_cast(U4, __builtin_amdgcn_raw_buffer_load_b128(xr, 16 * (lt + u * T), 0, 0));
+      m = max(m, key8(v[u]));
+    }
+    m = max64(m);
+    if constexpr (WPR > 1) {
+      if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) m = max(m, part[w]);
+      __syncthreads();                          // part is rewritten for the next row
+    }
+    if (live) {
+      const float scale = scale_from_amax(amax_from_key<DT>(m));
+      const bool fast = fast_scale(scale);
+      const float r = 1.0f / scale;
+      uint8_t* qr = q + row * cols;
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        const int64_t i = lt + u * T;
+        if (i < nv) *reinterpret_cast<uint2*>(qr + (i << 3)) = enc8<DT>(v[u], scale, r, fast);
+      }
+      if (lt == 0) scales[row] = scale;
+    }
+  }
+}
+
+// Rows longer than 16384 elements (VEC) or of any length (!VEC, rows not 16-byte aligned):
+// one workgroup per row, two passes - the amax, then the cast re-reading the row, which the
+// first pass has just brought into the caches.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void rows_two_pass_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t cols, uint8_t* __restrict__ q,
+                                                                 float* __restrict__ scales) {
+  __shared__ uint32_t part[kThreads / 64];
+  const int t = threadIdx.x;
+  const int64_t nv = VEC ? cols >> 3 : 0;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const uint16_t* xr = x + row * cols;
+    uint32_t m = 0;
+    int64_t i = t;
+    for (; i + 3 * kThreads < nv; i += 4 * kThreads) {   // four loads in flight per lane
+      const U4 v0 = load16(xr + (i << 3)), v1 = load16(xr + ((i + kThreads) << 3));
+      const U4 v2 = load16(xr + ((i + 2 * kThreads) << 3)), v3 = load16(xr + ((i + 3 * kThreads) << 3));
+      m = max(max(m, max(key8(v0), key8(v1))), max(key8(v2), key8(v3)));
+    }
+    for (; i < nv; i += kThreads) m = max(m, key8(load16(xr + (i << 3))));
+    for (int64_t j = (nv << 3) + t; j < cols; j += kThreads) m = max(m, xr[j] & 0x7fffu);
+    m = max64(m);
+    if ((t & 63) == 0) part[t >> 6] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) m = max(m, part[w]);
+    __syncthreads();
+    const float scale = scale_from_amax(amax_from_key<DT>(m));
+    const bool fast = fast_scale(scale);
+    const float r = 1.0f / scale;
+    uint8_t* qr = q + row * cols;
+    for (int64_t v = t; v < nv; v += kThreads)
+      *reinterpret_cast<uint2*>(qr + (v << 3)) = enc8<DT>(load16(xr + (v << 3)), scale, r, fast);
+    for (int64_t j = (nv << 3) + t; j < cols; j += kThreads) qr[j] = enc1<DT>(xr[j], scale, r, fast);
+    if (t == 0) scales[row] = scale;
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // 128x128 weight blocks: one workgroup per block.  Thread t owns columns
 // [8*(t%16), +8) of rows t/16 + 16*i, i = 0..7: eight 16-byte loads held in registers
 // through the block-wide reduction, then cast and stored.  VEC: cols % 8 == 0.
@@ -721,6 +816,35 @@ void launch_tensor_reduce_t(const void* x, int64_t n, float* word, bool want_sca
 }
 
 }  // namespace
+
+namespace {
+
+template <int DT>
+void launch_rows_t(const void* xv, int64_t rows, int64_t cols, uint8_t* q, float* scales, hipStream_t s) {
+  const uint16_t* x = static_cast<const uint16_t*>(xv);
+  constexpr int64_t kRowsCap = 256 * 64;       // workgroups; the kernels loop over further rows
+  if (cols % 8 != 0 || cols == 0) {           // (empty rows: scale 1, x and q never touched)
+    rows_two_pass_kernel<DT, false><<<grid_for(rows, 1, kRowsCap), kThreads, 0, s>>>(x, rows, cols, q, scales);
+    return;
+  }
+  const unsigned g_wave = grid_for(rows, kThreads / 64, kRowsCap);   // a row per wave
+  const unsigned g_wg = grid_for(rows, 1, kRowsCap);                  // a row per workgroup
+  if (cols <= 512) rows_vec_kernel<DT, 1, 1><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
+  else if (cols <= 1024) rows_vec_kernel<DT, 1, 2><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
+  else if (cols <= 2048) rows_vec_kernel<DT, 1, 4><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
+  else if (cols <= 4096) rows_vec_kernel<DT, 1, 8><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
+  else if (cols <= 8192) rows_vec_kernel<DT, 4, 4><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+  else if (cols <= 16384) rows_vec_kernel<DT, 4, 8><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+  else rows_two_pass_kernel<DT, true><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+}
+
+}  // namespace
+
+void launch_rows(int dt, const void* x, int64_t rows, int64_t cols, uint8_t* q, float* scales,
+                 hipStream_t s) {
+  if (dt == DT_BF16) launch_rows_t<DT_BF16>(x, rows, cols, q, scales, s);
+  else launch_rows_t<DT_F16>(x, rows, cols, q, scales, s);
+}
 
 void launch_groups(int dt, const void* x, int64_t rows, int64_t cols, int32_t group_rows,
                    uint8_t* q, float* out, bool write_q, hipStream_t s) {

@@ -171,6 +171,37 @@ fp8_status_t fp8_gemm_scaled_blockwise_ue8m0(const uint8_t* qa, const uint8_t* s
                                              void* c, fp8_dtype_t out_dt, void* stream);
 
 /*
+ * fp8_quantize_rowwise - per-channel scaling (Transformer Engine page, section 5: a scale
+ * per channel for the weights, beside per-tensor scaling; each scale as in section 3
+ * steps 2-4): one float32 scale per row,
+ *   scales[r] = amax(|x[r, :]|) / 448 (amax 0 -> 1.0, NaN -> NaN),
+ *   q[r, c]   = e4m3(x[r, c] / scales[r]), saturating round-to-nearest-even.
+ * For a weight W[N, K] a row is an output channel; for activations A[M, K] a row is a
+ * token (the per-token scales of fp8_gemm_scaled_rowwise).
+ *   x      : bf16/fp16 [rows, cols] row-major (device), 16-byte aligned.
+ *   q      : uint8 output [rows, cols] (device), 16-byte aligned; may be NULL when cols == 0.
+ *   scales : float32 output [rows] (device), 4-byte aligned.
+ * Errors: FP8_ERR_BAD_SHAPE (negative sizes), FP8_ERR_TOO_LARGE, FP8_ERR_BAD_DTYPE,
+ * FP8_ERR_NULL_POINTER, FP8_ERR_MISALIGNED, FP8_ERR_LAUNCH.  rows == 0 returns FP8_OK.
+ */
+fp8_status_t fp8_quantize_rowwise(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols, uint8_t* q,
+                                  float* scales, void* stream);
+
+/*
+ * fp8_gemm_scaled_rowwise - C = A @ B^T with one scale per token and per output channel
+ * (the per-channel scaling of the Transformer Engine page, section 5; product and scales as
+ * in its section 3 steps 5-6):
+ *   C[m, n] = out( sa[m] * sb[n] * sum_k qa[m, k] * qb[n, k] ), float32 accumulation.
+ *   sa : float32 [M] (device), e.g. from fp8_quantize_rowwise on A; a single per-tensor
+ *        activation scale is the case of M equal entries.
+ *   sb : float32 [N] (device), e.g. from fp8_quantize_rowwise on W.
+ * Other arguments, layout and errors: as fp8_gemm_scaled_tensorwise (K % 16 == 0).
+ */
+fp8_status_t fp8_gemm_scaled_rowwise(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                     const float* sb, int64_t M, int64_t N, int64_t K, void* c,
+                                     fp8_dtype_t out_dt, void* stream);
+
+/*
  * fp8_quantize_static - static scaling (the task page's FP8 recipe and calibration step: a
  * scale fixed before the pass instead of this tensor's amax): q = e4m3(x / *scale) in one
  * pass, saturating to +-448 where |x| > 448 * scale.

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(L):
                           "fp8_quantize_per_token_group", "fp8_gemm_scaled_tensorwise",
                           "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
                           "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0",
-                          "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed"}
+                          "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
+                          "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -45,7 +46,7 @@ def test_status_strings(L):
 
 
 @pytest.mark.parametrize("fn", ["fp8_gemm_scaled_tensorwise", "fp8_gemm_scaled_blockwise",
-                                "fp8_gemm_scaled_blockwise_ue8m0"])
+                                "fp8_gemm_scaled_blockwise_ue8m0", "fp8_gemm_scaled_rowwise"])
 def test_gemm_validation(L, fn):
     f = getattr(L, fn)
     good = (A16, A16, A16, A16)
@@ -121,6 +122,21 @@ def test_static_and_delayed_validation(L):
     assert up(A16, 8, A16, A16, 4, 127, A16, None) == SHAPE              # margin out of range
     assert up(None, 8, A16, A16, 4, 0, A16, None) == NULLP
     assert up(A16, 8, A16, A16 + 2, 4, 0, A16, None) == ALIGN
+
+
+def test_rowwise_quantize_validation(L):
+    f = L.fp8_quantize_rowwise
+    assert f(A16, 2, 4, 256, A16, A16, None) == DTYPE
+    assert f(A16, 0, -1, 256, A16, A16, None) == SHAPE
+    assert f(A16, 0, 4, -256, A16, A16, None) == SHAPE
+    assert f(None, 0, 0, 256, None, None, None) == OK                # no rows: nothing launched
+    assert f(A16, 0, 4, 256, A16, None, None) == NULLP               # scales are required
+    assert f(None, 0, 4, 256, A16, A16, None) == NULLP
+    assert f(A16, 0, 4, 256, None, A16, None) == NULLP
+    assert f(MIS, 0, 4, 256, A16, A16, None) == ALIGN
+    assert f(A16, 0, 4, 256, A16 + 8, A16, None) == ALIGN
+    assert f(A16, 0, 4, 256, A16, A16 + 2, None) == ALIGN
+    assert f(A16, 0, 1 << 31, 256, A16, A16, None) == LARGE
 
 
 def test_fused_delayed_validation(L):
