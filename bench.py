@@ -48,6 +48,9 @@ def parse():
                    help="per-tensor workloads: scale from this step's amax (dynamic), or the "
                         "delayed-scaling recipe (static cast with the scale left by the amax "
                         "history; margin 0, interval 4)")
+    p.add_argument("--rowwise", action="store_true",
+                   help="per-channel scaling on any workload shape: A per token every step, W per "
+                        "output channel once, the rowwise GEMM")
     p.add_argument("--scale-fmt", choices=["float32", "ue8m0"], default="float32",
                    help="blockwise workloads: float32 scales (amax/448) or UE8M0 power-of-two "
                         "scale bytes on the scaled MFMA")
@@ -71,11 +74,23 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload, M, scale_fmt="float32"):
-    return f"{workload}/M={M}" + ("/ue8m0" if scale_fmt == "ue8m0" else "")
+def scheme_of(w, scale_fmt="float32", act_scaling="dynamic", rowwise=False):
+    """How a step is scaled: tensorwise, tensorwise-delayed, blockwise, blockwise-ue8m0 or
+    rowwise."""
+    if rowwise:
+        return "rowwise"
+    if w.mode == "tensorwise":
+        return "tensorwise-delayed" if act_scaling == "delayed" else "tensorwise"
+    return "blockwise-ue8m0" if scale_fmt == "ue8m0" else "blockwise"
 
 
-def measured_traffic(workload, M, scale_fmt="float32"):
+def traffic_key(workload, M, scheme="tensorwise"):
+    """Counter-table key of a GEMM launch (delayed scaling runs the tensorwise GEMM)."""
+    suffix = {"blockwise-ue8m0": "/ue8m0", "rowwise": "/rowwise"}.get(scheme, "")
+    return f"{workload}/M={M}" + suffix
+
+
+def measured_traffic(workload, M, scheme="tensorwise"):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, or None when
     there is no entry for this workload or the kernel sources changed since it was taken."""
     import json as _json
@@ -84,7 +99,7 @@ def measured_traffic(workload, M, scale_fmt="float32"):
             table = _json.load(f)
     except (OSError, ValueError):
         return None
-    e = table.get(traffic_key(workload, M, scale_fmt))
+    e = table.get(traffic_key(workload, M, scheme))
     if not e or e.get("kernel_source_sha") != kernel_source_hash():
         return None
     return e.get("traffic_bytes_per_launch")
@@ -108,15 +123,18 @@ def copy_reference(mib, steps):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def algorithmic_bytes(w, M, scale_fmt="float32", act_scaling="dynamic"):
+def algorithmic_bytes(w, M, scheme="tensorwise"):
     """ABI-level bytes of one step: A read as bf16, qA written and read, scales, W read
     as FP8 with its scales, C written; plus B's quantize when it runs every call.  UE8M0
-    scales are one byte each in rows padded to four bytes.  Delayed scaling adds, per
-    delayed tensor, the recorded amax word and the update's history, step and scale."""
+    scales are one byte each in rows padded to four bytes; rowwise scales one float per
+    row of A and of W.  Delayed scaling adds, per delayed tensor, the recorded amax word
+    and the update's history, step and scale."""
     N, K = w.n, w.k
-    if w.mode == "tensorwise":
+    if scheme.startswith("tensorwise"):
         sa_bytes, sb_bytes = 4, 4
-    elif scale_fmt == "ue8m0":
+    elif scheme == "rowwise":
+        sa_bytes, sb_bytes = 4 * M, 4 * N
+    elif scheme == "blockwise-ue8m0":
         g4 = (K // 128 + 3) // 4 * 4
         sa_bytes, sb_bytes = M * g4, -(-N // 128) * g4
     else:
@@ -124,7 +142,7 @@ def algorithmic_bytes(w, M, scale_fmt="float32", act_scaling="dynamic"):
     quant_a = 2 * M * K + M * K + sa_bytes
     gemm = M * K + sa_bytes + N * K + sb_bytes + 2 * M * N
     quant_b = (2 * N * K + N * K + sb_bytes) if w.quantize_b_per_call else 0
-    if act_scaling == "delayed":
+    if scheme == "tensorwise-delayed":
         # beyond the cast (whose scale_used write is sa_bytes): the scale read by the cast, the
         # amax word (recorded, read, cleared), the history read, one entry written, the step
         # read and written, the scale read and rewritten
@@ -134,7 +152,7 @@ def algorithmic_bytes(w, M, scale_fmt="float32", act_scaling="dynamic"):
     return quant_a + gemm + quant_b, gemm
 
 
-def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32", act_scaling="dynamic"):
+def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
     """The oracle's quantize(A) + scaled GEMM on the host, on a row sample of A sized to
     roughly `budget_s` seconds; returns TFLOP/s (float64 arithmetic).  With delayed
     scaling the step is the oracle's static cast with the history's scale, its history
@@ -143,15 +161,17 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32", act_scal
     import oracle
     cores = len(os.sched_getaffinity(0))
     M, N, K = a_bits.shape[0], w.n, w.k
-    ue8m0 = scale_fmt == "ue8m0"
-    delayed = act_scaling == "delayed"
+    ue8m0 = scheme == "blockwise-ue8m0"
+    delayed = scheme == "tensorwise-delayed"
     if delayed:
         hist, step_a, scale_a = np.zeros(DELAYED_HISTORY, np.float32), 0, np.float32(1)
         amax_a = oracle.amax_per_tensor(oracle.input_to_f32(a_bits, "bf16"))
         for _ in range(DELAYED_INTERVAL):                      # reach the recipe's steady state
             hist, step_a, scale_a = oracle.delayed_step(hist, step_a, scale_a, amax_a, DELAYED_INTERVAL,
                                                         DELAYED_MARGIN)
-    if w.mode == "tensorwise":
+    if scheme == "rowwise":
+        qb, sb = oracle.quantize_rowwise(b_bits, "bf16")
+    elif w.mode == "tensorwise":
         qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
     elif ue8m0:
         qb, sb = oracle.quantize_groups_ue8m0(b_bits, "bf16", 128, 128)
@@ -163,7 +183,12 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32", act_scal
     while True:
         a = a_bits[:rows]
         t0 = time.perf_counter()
-        if w.mode == "tensorwise" and delayed:
+        if scheme == "rowwise":
+            qa, sa = oracle.quantize_rowwise(a, "bf16")
+            if w.quantize_b_per_call:
+                qb, sb = oracle.quantize_rowwise(b_bits, "bf16")
+            oracle.gemm_rowwise_ref(qa, sa, qb, sb)
+        elif delayed:
             qa, amax = oracle.quantize_static(a, "bf16", scale_a)
             oracle.delayed_step(hist, step_a, scale_a, amax, DELAYED_INTERVAL, DELAYED_MARGIN)
             if w.quantize_b_per_call:
@@ -192,7 +217,7 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scale_fmt="float32", act_scal
     flops = 2.0 * rows * N * K
     return {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"oracle {'delayed-scaling ' if delayed else ''}quantize(A[{rows},{K}]) + "
-                      f"{w.mode}{' UE8M0' if ue8m0 else ''} GEMM with W[{N},{K}], best of "
+                      f"{scheme} GEMM with W[{N},{K}], best of "
                       f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
 
 
@@ -228,6 +253,14 @@ def main():
     if delayed and blockwise:
         print(f"--act-scaling delayed is per-tensor scaling; {args.workload} is {w.mode}", file=sys.stderr)
         sys.exit(2)
+    rowwise = args.rowwise
+    if rowwise and (ue8m0 or delayed):
+        print("--rowwise replaces the workload's scaling; it takes neither --scale-fmt ue8m0 nor "
+              "--act-scaling delayed", file=sys.stderr)
+        sys.exit(2)
+    if rowwise:
+        blockwise = False                   # the workload's shape with per-row scales
+    scheme = scheme_of(w, args.scale_fmt, args.act_scaling, rowwise)
     ds_a = ds_b = None
     if delayed:
         # one delayed-scaling state per quantized tensor, shared by the rotation sets: the
@@ -238,7 +271,9 @@ def main():
 
     a0 = wl.bits_to_tensor(a_bits, device=dev)
     b0 = wl.bits_to_tensor(b_bits, device=dev)
-    if blockwise:
+    if rowwise:
+        qb0, sb0 = fp8.fp8_quantize_rowwise(b0)
+    elif blockwise:
         quant_groups = fp8.fp8_quantize_per_token_group_ue8m0 if ue8m0 else fp8.fp8_quantize_per_token_group
         qb0, sb0 = quant_groups(b0, 128, 128)
     else:
@@ -253,7 +288,13 @@ def main():
             s["b"] = b0.clone()
         else:
             s["qb"], s["sb"] = qb0.clone(), sb0.clone()
-        if blockwise:
+        if rowwise:
+            s["qa"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            s["sa"] = torch.empty((M,), dtype=torch.float32, device=dev)
+            if w.quantize_b_per_call:
+                s["qb"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
+                s["sb"] = torch.empty((N,), dtype=torch.float32, device=dev)
+        elif blockwise:
             s["qa"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
             s["sa"] = (torch.empty((M, fp8.e8m0_row_bytes(K // 128)), dtype=torch.uint8, device=dev) if ue8m0
                        else torch.empty((M, K // 128), dtype=torch.float32, device=dev))
@@ -267,7 +308,11 @@ def main():
     del a0, b0
 
     def quantize(s):
-        if blockwise:
+        if rowwise:
+            fp8.fp8_quantize_rowwise(s["a"], q=s["qa"], scales=s["sa"])
+            if w.quantize_b_per_call:
+                fp8.fp8_quantize_rowwise(s["b"], q=s["qb"], scales=s["sb"])
+        elif blockwise:
             quant_groups(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
         elif delayed:                       # cast, push the amax, refresh the scale: one launch
             ds_a.quantize_step(s["a"], q=s["qa"])
@@ -279,7 +324,9 @@ def main():
                 fp8.fp8_quantize_per_tensor(s["b"], q=s["qb"], scale=s["sb"])
 
     def gemm(s):
-        if blockwise:
+        if rowwise:
+            fp8.fp8_gemm_scaled_rowwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
+        elif blockwise:
             gemm_blockwise = fp8.fp8_gemm_scaled_blockwise_ue8m0 if ue8m0 else fp8.fp8_gemm_scaled_blockwise
             gemm_blockwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
         elif delayed:
@@ -348,7 +395,7 @@ def main():
     gemm_ms = gs.elapsed_time(ge) / (gemm_reps * R)
 
     flops = 2.0 * M * N * K
-    step_bytes, gemm_bytes = algorithmic_bytes(w, M, args.scale_fmt, args.act_scaling)
+    step_bytes, gemm_bytes = algorithmic_bytes(w, M, scheme)
     decode = M <= 16
     if decode:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -366,13 +413,14 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, M, args.scale_fmt)
+    roof["traffic"] = measured_traffic(args.workload, M, scheme)
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K_steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "scaling": w.mode,
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
+                   "scaling": "rowwise" if rowwise else w.mode,
                    "scale_fmt": args.scale_fmt if blockwise else "float32",
                    "act_scaling": args.act_scaling if not blockwise else "dynamic",
                    "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
@@ -384,8 +432,7 @@ def main():
         result["config"].update({"history": DELAYED_HISTORY, "interval": DELAYED_INTERVAL,
                                  "margin": DELAYED_MARGIN})
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scale_fmt=args.scale_fmt,
-                                              act_scaling=args.act_scaling)
+        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scheme=scheme)
     print(json.dumps(result), flush=True)
 
 

@@ -24,6 +24,32 @@ __device__ __forceinline__ float out_factor(float alpha, const float* sa, const 
   else return alpha;
 }
 
+// The same factors for the fragment layout of the 16x16 MFMA outputs (lane l holds token
+// row 16 i + l % 16 and output columns 16 j + 4 (l / 16) + r), loaded when a kernel starts
+// so that the loads overlap its K loop instead of following it.  Rows and columns past
+// the ends read the last entry (their outputs are not stored).
+template <int SM, int MI, int NJ>
+struct FragFactors {
+  static constexpr bool kRow = SM == SM_ROW;
+  float a[kRow ? MI : 1];
+  float b[kRow ? NJ : 1][4];
+  __device__ __forceinline__ void load(const float* sa, const float* sb, int m0, int n0, int M, int N) {
+    if constexpr (kRow) {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[i] = sa[min(m0 + 16 * i + (lane & 15), M - 1)];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[j][r] = sb[min(n0 + 16 * j + 4 * (lane >> 4) + r, N - 1)];
+    }
+  }
+  __device__ __forceinline__ float operator()(float alpha, int i, int j, int r) const {
+    if constexpr (kRow) return a[i] * b[j][r];
+    else return alpha;
+  }
+};
+
 // Exact float32 value of a 16-bit input pattern (low 16 bits of `h`).
 template <int DT>
 __device__ __forceinline__ float in_to_f32(uint32_t h) {

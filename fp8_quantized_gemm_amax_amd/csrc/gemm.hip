@@ -572,6 +572,8 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
   // ---- compute waves ----
   const int r16 = lane & 15, kq = lane >> 4;
   const int n0 = (blockIdx.x * cw + w) * 16 * NB;    // this wave's first weight row
+  FragFactors<SM, MB, NB> ff;                        // rowwise epilogue scales, fetched now
+  ff.load(sa, sb, 0, n0, M, N);
   // (readfirstlane keeps the clamp on the scalar unit: a VGPR range would make every
   // buffer load a waterfall loop)
   const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NB, N - n0)));
@@ -688,8 +690,7 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
       const int n = n0 + 16 * j + 4 * kq;
       uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * ff(alpha, b, j, r));
       if (vec_store && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {

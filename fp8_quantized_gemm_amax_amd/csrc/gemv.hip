@@ -79,6 +79,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   const int r16 = lane & 15, kq = lane >> 4;
   const int n0 = blockIdx.x * 16 * NB;
   const int nslabs = (K + kSlab - 1) / kSlab;
+  FragFactors<SM, MB, NB> ff;                                 // rowwise epilogue scales, fetched now
+  ff.load(sa, sb, 0, n0, M, N);
   const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
   const int KG4 = static_cast<int>(e8m0_row_bytes(KG));      // UE8M0: bytes per scale row
   const int SR = E8M0 ? KG4 : KG * 4;                         // bytes per scale row
@@ -224,8 +226,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
       const int n = n0 + 16 * j + 4 * kq;
       uint32_t h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_out_bits<OUT>(acc[j][b][r] * ff(alpha, b, j, r));
       if ((N & 3) == 0 && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
@@ -262,6 +263,11 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
   const int row0 = (blockIdx.x * 4 + w) * RPW;
   if (row0 >= N) return;                                      // no barrier in this kernel
   const int rows = min(RPW, N - row0);
+  // rowwise: the factor of the output this lane stores (lane m * RPW + r writes C[m, row0 + r]),
+  // fetched now so that the load overlaps the K loop
+  float row_factor = 1.0f;
+  if constexpr (SM == SM_ROW)
+    row_factor = sa[min(lane / RPW, M - 1)] * sb[row0 + min(lane % RPW, rows - 1)];
   const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
   const int SR = E8M0 ? static_cast<int>(e8m0_row_bytes(KG)) : KG * 4;   // bytes per scale row
   const int nch = (K + 1023) / 1024;
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
   const int m = lane / RPW, r = lane % RPW;
   if (lane < MT * RPW && m < M && r < rows)
     c[static_cast<int64_t>(m) * N + row0 + r] =
-        static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * out_factor<SM>(alpha, sa, sb, m, row0 + r)));
+        static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * (SM == SM_ROW ? row_factor : alpha)));
 }
 
 template <int BW, int OUT, int MT, int RPW, int UNROLL>

@@ -829,6 +829,15 @@ void launch_rows_t(const void* xv, int64_t rows, int64_t cols, uint8_t* q, float
   }
   const unsigned g_wave = grid_for(rows, kThreads / 64, kRowsCap);   // a row per wave
   const unsigned g_wg = grid_for(rows, 1, kRowsCap);                  // a row per workgroup
+  // few rows (decode tokens): a workgroup per row, so that each row has four times the loads
+  // in flight and no CU holds several of them
+  if (rows <= 256 && cols > 512 && cols <= 16384) {
+    if (cols <= 2048) rows_vec_kernel<DT, 4, 1><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+    else if (cols <= 4096) rows_vec_kernel<DT, 4, 2><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+    else if (cols <= 8192) rows_vec_kernel<DT, 4, 4><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+    else rows_vec_kernel<DT, 4, 8><<<g_wg, kThreads, 0, s>>>(x, rows, cols, q, scales);
+    return;
+  }
   if (cols <= 512) rows_vec_kernel<DT, 1, 1><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
   else if (cols <= 1024) rows_vec_kernel<DT, 1, 2><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
   else if (cols <= 2048) rows_vec_kernel<DT, 1, 4><<<g_wave, kThreads, 0, s>>>(x, rows, cols, q, scales);
