@@ -32,6 +32,11 @@ It is a plain, slow, obviously correct restatement of what the pages define:
   sa[m] * sb[n].  Source: the Transformer Engine page §5 (per-channel scaling of the
   weights) with §3 steps 2-6.
 
+* ``grouped`` - the mixture-of-experts grouped blockwise product: contiguous segments of
+  the routed activations, each multiplied by its expert's weight (float32 or UE8M0 block
+  scales).  Source: "FP8 chi tiết", its section on MoE experts (grouped_mm / batched_mm,
+  DeepGEMM expert kernels) with the opening bullets' block scaling.
+
 * ``delayed`` - static scaling (a scale fixed in advance; saturation) and the
   delayed-scaling amax history (max over the window, times 2^margin, every
   `interval` steps).  Source: the task page's DelayedScaling recipe and calibration
@@ -57,6 +62,8 @@ from .ue8m0 import (e8m0_decode, e8m0_from_amax, quantize_groups_ue8m0,
                     gemm_blockwise_ue8m0_ref, bound_blockwise_ue8m0)
 from .delayed import quantize_static, delayed_scale_from_history, delayed_step
 from .rowwise import amax_rows, quantize_rowwise, gemm_rowwise_ref, bound_rowwise
+from .grouped import (offsets_from_sizes, gemm_grouped_blockwise_ref, bound_grouped_blockwise,
+                      gemm_grouped_blockwise_ue8m0_ref, bound_grouped_blockwise_ue8m0)
 
 __all__ = [
     "E4M3_MAX", "decode_e4m3", "positive_values", "encode_e4m3", "nonneg_breakpoints",
@@ -67,4 +74,6 @@ __all__ = [
     "e8m0_decode", "e8m0_from_amax", "quantize_groups_ue8m0", "gemm_blockwise_ue8m0_ref",
     "bound_blockwise_ue8m0", "quantize_static", "delayed_scale_from_history", "delayed_step",
     "amax_rows", "quantize_rowwise", "gemm_rowwise_ref", "bound_rowwise",
+    "offsets_from_sizes", "gemm_grouped_blockwise_ref", "bound_grouped_blockwise",
+    "gemm_grouped_blockwise_ue8m0_ref", "bound_grouped_blockwise_ue8m0",
 ]
