@@ -10,6 +10,7 @@ from .binding import (Fp8Error, fp8_amax, fp8_quantize_per_tensor, fp8_quantize_
                       fp8_quantize_per_token_group_ue8m0, fp8_gemm_scaled_blockwise_ue8m0,
                       e8m0_row_bytes, fp8_quantize_static, fp8_delayed_scaling_update, fp8_quantize_delayed,
                       DelayedScaling, fp8_quantize_rowwise, fp8_gemm_scaled_rowwise,
+                      fp8_gemm_grouped_blockwise, fp8_gemm_grouped_blockwise_ue8m0,
                       lib, LIB_PATH)
 
 __all__ = ["Fp8Error", "fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_per_token_group",
@@ -17,4 +18,5 @@ __all__ = ["Fp8Error", "fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_per_
            "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0", "e8m0_row_bytes",
            "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
            "DelayedScaling", "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise",
+           "fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0",
            "lib", "LIB_PATH"]

@@ -34,6 +34,10 @@ _SIGNATURES = {
     "fp8_gemm_scaled_blockwise_ue8m0": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "fp8_quantize_rowwise": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_gemm_scaled_rowwise": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "fp8_gemm_grouped_blockwise": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_int, _P],
+                                   ctypes.c_int),
+    "fp8_gemm_grouped_blockwise_ue8m0": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_int, _P],
+                                         ctypes.c_int),
     "fp8_quantize_static": ([_P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "fp8_delayed_scaling_update": ([_P, _I32, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "fp8_quantize_delayed": ([_P, ctypes.c_int, _I64, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P],
@@ -242,6 +246,48 @@ def fp8_gemm_scaled_rowwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
     if sa.numel() != M or sb.numel() != N:
         raise ValueError(f"rowwise scales must have {M} and {N} entries, got {sa.numel()} and {sb.numel()}")
     return _gemm("fp8_gemm_scaled_rowwise", qa, sa, qb, sb, out_dtype, out)
+
+
+def _grouped(name, qa, sa, qb, sb, offsets, out_dtype, out, scale_dtype):
+    qa = _codes(_as_2d(qa))
+    qb = _codes(qb)
+    if qb.dim() != 3:
+        raise ValueError(f"expert weights must be [E, N, K], got {tuple(qb.shape)}")
+    qb = qb.contiguous()
+    _need_cuda(qa, qb, sa, sb, offsets)
+    T, K = qa.shape
+    E, N, K2 = qb.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: qa has {K}, qb has {K2}")
+    if offsets.dtype != torch.int32 or offsets.numel() != E + 1:
+        raise TypeError(f"offsets must be int32 [{E + 1}]")
+    sa, sb, offsets = sa.contiguous(), sb.contiguous(), offsets.contiguous()
+    if sa.dtype != scale_dtype or sb.dtype != scale_dtype:
+        raise TypeError(f"scales must be {scale_dtype}")
+    if K % 128 == 0 and K > 0:
+        g = K // 128 if scale_dtype == torch.float32 else e8m0_row_bytes(K // 128)
+        if tuple(sa.shape) != (T, g) or tuple(sb.shape) != (E, -(-N // 128), g):
+            raise ValueError(f"grouped scales must be [{T}, {g}] and [{E}, {-(-N // 128)}, {g}], "
+                             f"got {tuple(sa.shape)} and {tuple(sb.shape)}")
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype, device=qa.device)
+    _need_cuda(out)
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(offsets), E, T, N, K, _ptr(out),
+                    _out_dt(out.dtype), _stream(qa)))
+    return out
+
+
+def fp8_gemm_grouped_blockwise(qa, sa, qb, sb, offsets, out_dtype=torch.bfloat16, out=None):
+    """Mixture-of-experts product: rows offsets[e]:offsets[e+1] of qa [T, K] times expert
+    weight qb[e] ([E, N, K]); sa float32 [T, K/128], sb float32 [E, ceil(N/128), K/128],
+    offsets int32 [E + 1] on the device.  Returns C [T, N]."""
+    return _grouped("fp8_gemm_grouped_blockwise", qa, sa, qb, sb, offsets, out_dtype, out, torch.float32)
+
+
+def fp8_gemm_grouped_blockwise_ue8m0(qa, sa, qb, sb, offsets, out_dtype=torch.bfloat16, out=None):
+    """The grouped product with UE8M0 scales: sa uint8 [T, G4], sb uint8 [E, ceil(N/128), G4]."""
+    return _grouped("fp8_gemm_grouped_blockwise_ue8m0", qa, sa, qb, sb, offsets, out_dtype, out, torch.uint8)
 
 
 def fp8_gemm_scaled_blockwise(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):

@@ -11,6 +11,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;   // kernels index rows/cols with int
 constexpr int64_t kMaxElems = int64_t{1} << 40;
+constexpr int64_t kMaxExperts = int64_t{1} << 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -45,6 +46,25 @@ fp8_status_t gemm_common(int mode, const uint8_t* qa, const void* sa, const uint
   fp8amax::launch_gemm(mode, static_cast<int>(out_dt), qa, sa, qb, sb, static_cast<int>(M),
                        static_cast<int>(N), static_cast<int>(K), c,
                        static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+fp8_status_t grouped_common(int mode, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb,
+                            const int32_t* offsets, int64_t E, int64_t T, int64_t N, int64_t K, void* c,
+                            fp8_dtype_t out_dt, void* stream) {
+  if (E < 1 || T < 0 || N < 0 || K <= 0 || K % 128 != 0) return FP8_ERR_BAD_SHAPE;
+  if (E > kMaxExperts || T > kMaxDim || N > kMaxDim || K * 256 >= (int64_t{1} << 31)) return FP8_ERR_TOO_LARGE;
+  if (E * N > kMaxDim || (N > 0 && E > kMaxElems / (N * K))) return FP8_ERR_TOO_LARGE;
+  if (!valid_dt(out_dt)) return FP8_ERR_BAD_DTYPE;
+  if (T == 0 || N == 0) return FP8_OK;
+  if (!qa || !sa || !qb || !sb || !offsets || !c) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(qa) || !aligned16(qb) || !aligned16(c) || !aligned4(sa) || !aligned4(sb) || !aligned4(offsets))
+    return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  if (!fp8amax::launch_grouped(mode, static_cast<int>(out_dt), qa, sa, qb, sb, offsets, static_cast<int>(E),
+                               static_cast<int>(T), static_cast<int>(N), static_cast<int>(K), c,
+                               static_cast<hipStream_t>(stream)))
+    return FP8_ERR_TOO_LARGE;
   return finish_launch();
 }
 
@@ -114,6 +134,18 @@ fp8_status_t fp8_gemm_scaled_rowwise(const uint8_t* qa, const float* sa, const u
                                      const float* sb, int64_t M, int64_t N, int64_t K, void* c,
                                      fp8_dtype_t out_dt, void* stream) {
   return gemm_common(fp8amax::SM_ROW, qa, sa, qb, sb, M, N, K, c, out_dt, stream);
+}
+
+fp8_status_t fp8_gemm_grouped_blockwise(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+                                       const int32_t* offsets, int64_t E, int64_t T, int64_t N, int64_t K,
+                                       void* c, fp8_dtype_t out_dt, void* stream) {
+  return grouped_common(fp8amax::SM_BLOCK, qa, sa, qb, sb, offsets, E, T, N, K, c, out_dt, stream);
+}
+
+fp8_status_t fp8_gemm_grouped_blockwise_ue8m0(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
+                                             const uint8_t* sb, const int32_t* offsets, int64_t E, int64_t T,
+                                             int64_t N, int64_t K, void* c, fp8_dtype_t out_dt, void* stream) {
+  return grouped_common(fp8amax::SM_E8M0, qa, sa, qb, sb, offsets, E, T, N, K, c, out_dt, stream);
 }
 
 fp8_status_t fp8_quantize_per_token_group(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,

@@ -511,22 +511,35 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
 // The launch has cw + 1 waves (cw <= kSkinnyMaxCw): the number of compute waves sets how
 // many weight rows a workgroup covers, and is chosen so one round of workgroups spans N.
 constexpr int kSkinnyMaxCw = 7;
+
+template <int SM, int MB>
+struct SkinnyShape {
+  static constexpr bool BLOCKWISE = slab_scaled(SM);
+  static constexpr int IA = 2 * MB;                          // A DMA instructions per slab (8 rows each)
+  static constexpr int IS = BLOCKWISE ? (16 * MB + 63) / 64 : 0;   // scale DMA instructions (64 rows each)
+  static constexpr int PER = IA + IS;
+  static constexpr int A_BYTES = 16 * MB * kSlab;            // one stage of the A ring
+  static constexpr int S_FLOATS = BLOCKWISE ? IS * 64 : 1;   // one stage of the scale ring
+};
+
+// The few-token product of one workgroup: A rows [0, M) (M <= 16 MB) times the 16 cw NB
+// weight rows of block `nblk`, written to C rows [0, M).  Abuf and Sbuf are the workgroup's
+// LDS rings; every wave of the workgroup calls this once per tile, and each call passes
+// exactly K / 128 barriers in every wave.
 template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
-__global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
+__device__ __forceinline__ void skinny_body(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
-    const void* __restrict__ sb_, int M, int N, int K, int cw, uint16_t* __restrict__ c) {
+    const void* __restrict__ sb_, int M, int N, int K, int cw, uint16_t* __restrict__ c, int nblk,
+    uint8_t (*Abuf)[SkinnyShape<SM, MB>::A_BYTES], float (*Sbuf)[SkinnyShape<SM, MB>::S_FLOATS]) {
   constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
   const float* __restrict__ sb = static_cast<const float*>(sb_);
-  constexpr int IA = 2 * MB;                         // A DMA instructions per slab (8 rows each)
-  constexpr int IS = BLOCKWISE ? (16 * MB + 63) / 64 : 0;   // scale DMA instructions (64 rows each)
-  constexpr int PER = IA + IS;
+  constexpr int IA = SkinnyShape<SM, MB>::IA;
+  constexpr int IS = SkinnyShape<SM, MB>::IS;
+  constexpr int PER = SkinnyShape<SM, MB>::PER;
   static_assert(NS >= 2 && (NS - 2) * PER < 64, "slabs in flight fit vmcnt");
   static_assert(kSlab % (16 * NB) == 0, "a wave's rows share one weight block");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][16 * MB * kSlab];
-  __shared__ __attribute__((aligned(16))) float Sbuf[NS][BLOCKWISE ? IS * 64 : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -571,7 +584,7 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
 
   // ---- compute waves ----
   const int r16 = lane & 15, kq = lane >> 4;
-  const int n0 = (blockIdx.x * cw + w) * 16 * NB;    // this wave's first weight row
+  const int n0 = (nblk * cw + w) * 16 * NB;          // this wave's first weight row
   FragFactors<SM, MB, NB> ff;                        // rowwise epilogue scales, fetched now
   ff.load(sa, sb, 0, n0, M, N);
   // (readfirstlane keeps the clamp on the scalar unit: a VGPR range would make every
@@ -703,6 +716,87 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
 }
 
 template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
+__global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb, int M, int N, int K, int cw, uint16_t* __restrict__ c) {
+  using Shape = SkinnyShape<SM, MB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][Shape::A_BYTES];
+  __shared__ __attribute__((aligned(16))) float Sbuf[NS][Shape::S_FLOATS];
+  skinny_body<SM, OUT, NB, MB, NS, UNROLL>(qa, sa, qb, sb, M, N, K, cw, c, blockIdx.x, Abuf, Sbuf);
+}
+
+// Grouped (mixture-of-experts) product: expert e's tokens are the rows
+// [offsets[e], offsets[e + 1]) of A and C, multiplied by its weight qb[e] with its block
+// scales (the fine-grained FP8 page's expert products).  Each workgroup takes one tile:
+// chunk j of 16 MB consecutive tokens of one expert, times weight block `nblk` of that
+// expert (16 cw NB rows).  Its first wave finds the tile from the offsets alone - the
+// number of chunks of each expert, prefix-summed 64 experts at a time - so the group sizes
+// never go to the host and the launch can be captured in a graph.  The grid is sized for
+// the worst case (sum_e ceil(m_e / chunk) <= T / chunk + E); workgroups past the last tile
+// return before their first barrier.  Offsets are clamped to [0, T] and an expert whose end
+// lies before its start is empty, so any offsets give in-bounds accesses.
+template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
+__global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_grouped_kernel(
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb, const int* __restrict__ offsets, int E, int T, int N, int K, int cw,
+    int nblks, uint16_t* __restrict__ c) {
+  using Shape = SkinnyShape<SM, MB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][Shape::A_BYTES];
+  __shared__ __attribute__((aligned(16))) float Sbuf[NS][Shape::S_FLOATS];
+  __shared__ int tile[3];                           // expert (-1: none), first row, rows
+  constexpr int CH = 16 * MB;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int chunk = blockIdx.x / nblks;
+    int base = 0, found = -1, row0 = 0, rows = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {            // uniform loop
+      const int e = e0 + lane;
+      int lo = 0, m = 0;
+      if (e < E) {
+        lo = min(max(offsets[e], 0), T);
+        m = min(max(offsets[e + 1], lo), T) - lo;
+      }
+      const int n_ch = (m + CH - 1) / CH;
+      int incl = n_ch;                              // inclusive prefix over the 64 experts
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const int first = base + incl - n_ch;         // this expert's first chunk
+      const bool mine = chunk >= first && chunk < base + incl;
+      const uint64_t hit = __ballot(mine);
+      if (hit) {
+        const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        const int j = chunk - first;                // chunk within the expert
+        found = __shfl(e, src, 64);
+        row0 = __shfl(lo + j * CH, src, 64);
+        rows = __shfl(min(CH, m - j * CH), src, 64);
+        break;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+      tile[0] = found;
+      tile[1] = row0;
+      tile[2] = rows;
+    }
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(tile[0]);
+  if (e < 0) return;                                // every wave alike, before any barrier
+  const int row0 = __builtin_amdgcn_readfirstlane(tile[1]);
+  const int rows = __builtin_amdgcn_readfirstlane(tile[2]);
+  const int KG = K / kSlab;
+  const int64_t sa_row = SM == SM_E8M0 ? e8m0_row_bytes(KG) : int64_t{4} * KG;   // bytes per scale row
+  const int64_t sb_rows = (N + kSlab - 1) / kSlab;
+  skinny_body<SM, OUT, NB, MB, NS, UNROLL>(
+      qa + static_cast<int64_t>(row0) * K, static_cast<const uint8_t*>(sa) + row0 * sa_row,
+      qb + static_cast<int64_t>(e) * N * K, static_cast<const uint8_t*>(sb) + e * sb_rows * sa_row,
+      rows, N, K, cw, c + static_cast<int64_t>(row0) * N, blockIdx.x % nblks, Abuf, Sbuf);
+}
+
+template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
 void launch_skinny(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                    int K, int cw, void* c, hipStream_t s) {
   const int rows = 16 * cw * NB;
@@ -766,6 +860,26 @@ void launch_gemm_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const v
   else launch_dma<128, 128, 64, 32, SM, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
+// Grouped launch: 16 MB tokens per chunk, cw compute waves of NB weight-row blocks each.
+// Returns false when the worst-case grid does not fit a launch.
+template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
+bool launch_grouped_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, const int* offsets,
+                      int E, int T, int N, int K, int cw, void* c, hipStream_t s) {
+  const int rows = 16 * cw * NB;
+  const int64_t nblks = (N + rows - 1) / rows;
+  const int64_t chunks = (static_cast<int64_t>(T) + 16 * MB - 1) / (16 * MB) + E;
+  if (chunks * nblks > (int64_t{1} << 31) - 1) return false;
+  gemm_grouped_kernel<SM, OUT, NB, MB, NS, UNROLL><<<static_cast<unsigned>(chunks * nblks), (cw + 1) * 64, 0, s>>>(
+      qa, sa, qb, sb, offsets, E, T, N, K, cw, static_cast<int>(nblks), static_cast<uint16_t*>(c));
+  return true;
+}
+
+template <int SM, int OUT>
+bool launch_grouped_m(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, const int* offsets,
+                      int E, int T, int N, int K, void* c, hipStream_t s) {
+  return launch_grouped_t<SM, OUT, 2, 8, 5, 2>(qa, sa, qb, sb, offsets, E, T, N, K, 7, c, s);
+}
+
 template <int SM>
 void launch_gemm_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M,
                    int N, int K, void* c, hipStream_t s) {
@@ -774,6 +888,15 @@ void launch_gemm_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t*
 }
 
 }  // namespace
+
+bool launch_grouped(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb,
+                    const int* offsets, int E, int T, int N, int K, void* c, hipStream_t s) {
+  if (mode == SM_E8M0)
+    return out_dt == DT_BF16 ? launch_grouped_m<SM_E8M0, DT_BF16>(qa, sa, qb, sb, offsets, E, T, N, K, c, s)
+                             : launch_grouped_m<SM_E8M0, DT_F16>(qa, sa, qb, sb, offsets, E, T, N, K, c, s);
+  return out_dt == DT_BF16 ? launch_grouped_m<SM_BLOCK, DT_BF16>(qa, sa, qb, sb, offsets, E, T, N, K, c, s)
+                           : launch_grouped_m<SM_BLOCK, DT_F16>(qa, sa, qb, sb, offsets, E, T, N, K, c, s);
+}
 
 void launch_gemm(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
                  const void* sb, int M, int N, int K, void* c, hipStream_t s) {

@@ -202,6 +202,44 @@ fp8_status_t fp8_gemm_scaled_rowwise(const uint8_t* qa, const float* sa, const u
                                      fp8_dtype_t out_dt, void* stream);
 
 /*
+ * fp8_gemm_grouped_blockwise - the mixture-of-experts product of the fine-grained FP8 page
+ * (its section on MoE experts: grouped_mm / batched_mm with float32 scales; the block
+ * scaling of its opening bullets): E experts, each with its own weight, and the routed
+ * tokens already permuted into one contiguous segment per expert.  For every expert e and
+ * every row t in [offsets[e], offsets[e + 1]):
+ *   C[t, n] = out( sum_g sa[t, g] * sb[e, n / 128, g] * sum_{k in slab g} qa[t, k] * qb[e, n, k] )
+ *   qa      : uint8 e4m3 [T, K] (device), the permuted activations (a token sent to k experts
+ *             appears k times), e.g. from fp8_quantize_per_token_group (1 x 128).
+ *   sa      : float32 [T, K/128] (device).
+ *   qb      : uint8 e4m3 [E, N, K] (device), the experts' weights, each row-major [N, K].
+ *   sb      : float32 [E, ceil(N/128), K/128] (device), each expert's 128 x 128 block scales.
+ *   offsets : int32 [E + 1] (device), non-decreasing, offsets[0] = 0, offsets[E] = T.  They
+ *             stay on the device (no host synchronisation; the call can be captured in a HIP
+ *             graph).  Values outside [0, T] are clamped and an expert whose end precedes its
+ *             start is empty, so any offsets give in-bounds accesses; rows of C that no
+ *             segment covers are not written, rows covered twice get either result.
+ *   c       : bf16/fp16 output [T, N] (device), 16-byte aligned.
+ * Requires E >= 1 (at most 65536), K % 128 == 0 and K > 0; T == 0 or N == 0 returns FP8_OK.
+ * qa, qb and c need 16-byte alignment, sa, sb and offsets 4-byte alignment.  Errors:
+ * FP8_ERR_BAD_SHAPE, FP8_ERR_TOO_LARGE, FP8_ERR_BAD_DTYPE, FP8_ERR_NULL_POINTER,
+ * FP8_ERR_MISALIGNED, FP8_ERR_LAUNCH.
+ */
+fp8_status_t fp8_gemm_grouped_blockwise(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+                                       const int32_t* offsets, int64_t E, int64_t T, int64_t N, int64_t K,
+                                       void* c, fp8_dtype_t out_dt, void* stream);
+
+/*
+ * fp8_gemm_grouped_blockwise_ue8m0 - fp8_gemm_grouped_blockwise with UE8M0 scales (the same
+ * page: the newest DeepGEMM expert kernels take only e8m0fnu scale bytes):
+ *   sa : uint8 e8m0fnu [T, G4];  sb : uint8 e8m0fnu [E, ceil(N/128), G4], G4 = K/128 rounded
+ *        up to a multiple of 4 (the layout fp8_quantize_per_token_group_ue8m0 writes).
+ * Everything else as fp8_gemm_grouped_blockwise.
+ */
+fp8_status_t fp8_gemm_grouped_blockwise_ue8m0(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
+                                             const uint8_t* sb, const int32_t* offsets, int64_t E, int64_t T,
+                                             int64_t N, int64_t K, void* c, fp8_dtype_t out_dt, void* stream);
+
+/*
  * fp8_quantize_static - static scaling (the task page's FP8 recipe and calibration step: a
  * scale fixed before the pass instead of this tensor's amax): q = e4m3(x / *scale) in one
  * pass, saturating to +-448 where |x| > 448 * scale.

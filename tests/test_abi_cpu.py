@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(L):
                           "fp8_gemm_scaled_blockwise", "fp8_debug_cast_f32",
                           "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0",
                           "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
-                          "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise"}
+                          "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise",
+                          "fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -122,6 +123,30 @@ def test_static_and_delayed_validation(L):
     assert up(A16, 8, A16, A16, 4, 127, A16, None) == SHAPE              # margin out of range
     assert up(None, 8, A16, A16, 4, 0, A16, None) == NULLP
     assert up(A16, 8, A16, A16 + 2, 4, 0, A16, None) == ALIGN
+
+
+@pytest.mark.parametrize("fn", ["fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0"])
+def test_grouped_validation(L, fn):
+    """(qa, sa, qb, sb, offsets, E, T, N, K, c, out_dt, stream)"""
+    f = getattr(L, fn)
+
+    def call(qa=A16, sa=A16, qb=A16, sb=A16, off=A16, E=4, T=64, N=256, K=256, c=A16, dt=0):
+        return f(qa, sa, qb, sb, off, E, T, N, K, c, dt, None)
+
+    assert call(E=0) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(K=200) == SHAPE
+    assert call(K=0) == SHAPE
+    assert call(E=1 << 17) == LARGE
+    assert call(K=1 << 24) == LARGE
+    assert call(dt=9) == DTYPE
+    assert call(T=0, qa=None, off=None) == OK                       # nothing to compute
+    assert call(N=0) == OK
+    assert call(off=None) == NULLP
+    assert call(sb=None) == NULLP
+    assert call(qa=MIS) == ALIGN
+    assert call(off=A16 + 2) == ALIGN
+    assert call(c=A16 + 8) == ALIGN
 
 
 def test_rowwise_quantize_validation(L):
