@@ -79,6 +79,8 @@ def scheme_of(w, scale_fmt="float32", act_scaling="dynamic", rowwise=False):
     rowwise."""
     if rowwise:
         return "rowwise"
+    if w.mode == "grouped":
+        return "grouped-ue8m0" if scale_fmt == "ue8m0" else "grouped"
     if w.mode == "tensorwise":
         return "tensorwise-delayed" if act_scaling == "delayed" else "tensorwise"
     return "blockwise-ue8m0" if scale_fmt == "ue8m0" else "blockwise"
@@ -86,7 +88,7 @@ def scheme_of(w, scale_fmt="float32", act_scaling="dynamic", rowwise=False):
 
 def traffic_key(workload, M, scheme="tensorwise"):
     """Counter-table key of a GEMM launch (delayed scaling runs the tensorwise GEMM)."""
-    suffix = {"blockwise-ue8m0": "/ue8m0", "rowwise": "/rowwise"}.get(scheme, "")
+    suffix = {"blockwise-ue8m0": "/ue8m0", "grouped-ue8m0": "/ue8m0", "rowwise": "/rowwise"}.get(scheme, "")
     return f"{workload}/M={M}" + suffix
 
 
@@ -130,6 +132,12 @@ def algorithmic_bytes(w, M, scheme="tensorwise"):
     row of A and of W.  Delayed scaling adds, per delayed tensor, the recorded amax word
     and the update's history, step and scale."""
     N, K = w.n, w.k
+    if w.mode == "grouped":                 # B is every expert's weight and block scales
+        g = (K // 128 + 3) // 4 * 4 if scheme == "grouped-ue8m0" else 4 * (K // 128)
+        sa_bytes, sb_bytes = M * g, w.experts * -(-N // 128) * g
+        quant_a = 2 * M * K + M * K + sa_bytes
+        gemm = M * K + sa_bytes + w.experts * N * K + sb_bytes + 2 * M * N + 4 * (w.experts + 1)
+        return quant_a + gemm, gemm
     if scheme.startswith("tensorwise"):
         sa_bytes, sb_bytes = 4, 4
     elif scheme == "rowwise":
@@ -161,6 +169,8 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
     import oracle
     cores = len(os.sched_getaffinity(0))
     M, N, K = a_bits.shape[0], w.n, w.k
+    if w.mode == "grouped":
+        return cpu_baseline_grouped(w, a_bits, scheme, cores)
     ue8m0 = scheme == "blockwise-ue8m0"
     delayed = scheme == "tensorwise-delayed"
     if delayed:
@@ -221,6 +231,33 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
                       f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
 
 
+def cpu_baseline_grouped(w, a_bits, scheme, cores):
+    """The oracle's quantize + grouped product on a bounded sample: the rows routed to
+    expert 0 (its weight quantized beforehand, as the GPU step does)."""
+    import numpy as np
+    import oracle
+    from fp8_quantized_gemm_amax_amd import workloads as wl
+    M, N, K = a_bits.shape[0], w.n, w.k
+    sizes = wl.group_sizes(w.name, M)
+    rows = int(sizes[0])
+    ue8m0 = scheme == "grouped-ue8m0"
+    quant = oracle.quantize_groups_ue8m0 if ue8m0 else oracle.quantize_groups
+    gemm = oracle.gemm_grouped_blockwise_ue8m0_ref if ue8m0 else oracle.gemm_grouped_blockwise_ref
+    qb, sb = quant(wl.expert_weight_bits(w.name, 0), "bf16", 128, 128)
+    off = np.array([0, rows])
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        qa, sa = quant(a_bits[:rows], "bf16", 1, 128)
+        gemm(qa, sa, qb[None], sb[None], off)
+        runs.append(time.perf_counter() - t0)
+    best = min(runs)
+    return {"value": round(2.0 * rows * N * K / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"oracle quantize + {scheme} product of the {rows} rows routed to expert 0 "
+                      f"(W_0[{N},{K}]), best of 3 ({best:.2f} s); float64 NumPy, {cores} host threads"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,8 +282,12 @@ def main():
     a_bits, b_bits = wl.make_inputs(args.workload, M)
     out_dtype = torch.float16 if w.out_dtype == "f16" else torch.bfloat16
     blockwise = w.mode == "blockwise"
+    grouped = w.mode == "grouped"
     ue8m0 = args.scale_fmt == "ue8m0"
-    if ue8m0 and not blockwise:
+    if grouped and (args.rowwise or args.act_scaling == "delayed"):
+        print(f"{args.workload} is a grouped (expert) workload with block scales only", file=sys.stderr)
+        sys.exit(2)
+    if ue8m0 and not (blockwise or grouped):
         print(f"--scale-fmt ue8m0 needs a blockwise workload; {args.workload} is {w.mode}", file=sys.stderr)
         sys.exit(2)
     delayed = args.act_scaling == "delayed"
@@ -270,8 +311,10 @@ def main():
             ds_b = fp8.DelayedScaling(DELAYED_HISTORY, DELAYED_INTERVAL, DELAYED_MARGIN, device=dev)
 
     a0 = wl.bits_to_tensor(a_bits, device=dev)
-    b0 = wl.bits_to_tensor(b_bits, device=dev)
-    if rowwise:
+    b0 = wl.bits_to_tensor(b_bits, device=dev) if b_bits is not None else None
+    if grouped:
+        pass
+    elif rowwise:
         qb0, sb0 = fp8.fp8_quantize_rowwise(b0)
     elif blockwise:
         quant_groups = fp8.fp8_quantize_per_token_group_ue8m0 if ue8m0 else fp8.fp8_quantize_per_token_group
@@ -279,10 +322,32 @@ def main():
     else:
         qb0, sb0 = fp8.fp8_quantize_per_tensor(b0)
 
-    per_set = 2 * M * K + M * K + 2 * M * N + N * K + (2 * N * K if w.quantize_b_per_call else 0)
+    if grouped:
+        # every expert's weight drawn and quantized on the GPU once (128 x 128 blocks), shared
+        # by all steps: at 0.94 GB it is read from HBM on every step; the routed rows rotate
+        E = w.experts
+        sizes = wl.group_sizes(args.workload, M)
+        offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)).to(dev)
+        quant_groups = fp8.fp8_quantize_per_token_group_ue8m0 if ue8m0 else fp8.fp8_quantize_per_token_group
+        g = fp8.e8m0_row_bytes(K // 128) if ue8m0 else K // 128
+        qb0 = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        sb0 = torch.empty((E, -(-N // 128), g), dtype=torch.uint8 if ue8m0 else torch.float32, device=dev)
+        for e in range(E):
+            be = wl.bits_to_tensor(wl.expert_weight_bits(args.workload, e), device=dev)
+            quant_groups(be, 128, 128, q=qb0[e], scales=sb0[e])
+            del be
+        gemm_grouped = fp8.fp8_gemm_grouped_blockwise_ue8m0 if ue8m0 else fp8.fp8_gemm_grouped_blockwise
+        per_set = 2 * M * K + M * K + 2 * M * N
+    else:
+        per_set = 2 * M * K + M * K + 2 * M * N + N * K + (2 * N * K if w.quantize_b_per_call else 0)
     R = max(2, min(256, -(-ROTATION_BYTES // per_set)))
     sets = []
     for _ in range(R):
+        if grouped:
+            sets.append({"a": a0.clone(), "c": torch.empty((M, N), dtype=out_dtype, device=dev),
+                         "qa": torch.empty((M, K), dtype=torch.uint8, device=dev),
+                         "sa": torch.empty((M, g), dtype=torch.uint8 if ue8m0 else torch.float32, device=dev)})
+            continue
         s = {"a": a0.clone(), "c": torch.empty((M, N), dtype=out_dtype, device=dev)}
         if w.quantize_b_per_call:
             s["b"] = b0.clone()
@@ -308,7 +373,9 @@ def main():
     del a0, b0
 
     def quantize(s):
-        if rowwise:
+        if grouped:
+            quant_groups(s["a"], 1, 128, q=s["qa"], scales=s["sa"])
+        elif rowwise:
             fp8.fp8_quantize_rowwise(s["a"], q=s["qa"], scales=s["sa"])
             if w.quantize_b_per_call:
                 fp8.fp8_quantize_rowwise(s["b"], q=s["qb"], scales=s["sb"])
@@ -324,7 +391,9 @@ def main():
                 fp8.fp8_quantize_per_tensor(s["b"], q=s["qb"], scale=s["sb"])
 
     def gemm(s):
-        if rowwise:
+        if grouped:
+            gemm_grouped(s["qa"], s["sa"], qb0, sb0, offsets, out=s["c"])
+        elif rowwise:
             fp8.fp8_gemm_scaled_rowwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
         elif blockwise:
             gemm_blockwise = fp8.fp8_gemm_scaled_blockwise_ue8m0 if ue8m0 else fp8.fp8_gemm_scaled_blockwise
@@ -421,7 +490,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K,
                    "scaling": "rowwise" if rowwise else w.mode,
-                   "scale_fmt": args.scale_fmt if blockwise else "float32",
+                   "scale_fmt": args.scale_fmt if (blockwise or grouped) else "float32",
                    "act_scaling": args.act_scaling if not blockwise else "dynamic",
                    "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
                    "gemm_ms": round(gemm_ms, 6), "host_s": round(host_s, 4),
@@ -431,6 +500,9 @@ def main():
     if delayed:
         result["config"].update({"history": DELAYED_HISTORY, "interval": DELAYED_INTERVAL,
                                  "margin": DELAYED_MARGIN})
+    if grouped:
+        result["config"].update({"experts": w.experts, "rows_per_expert_min": int(sizes.min()),
+                                 "rows_per_expert_max": int(sizes.max())})
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scheme=scheme)
     print(json.dumps(result), flush=True)

@@ -30,6 +30,7 @@ class Workload:
     out_dtype: str           # "bf16" or "f16"
     quantize_b_per_call: bool
     description: str
+    experts: int = 0         # grouped workloads: experts on this GPU (B is [experts * n, k])
 
 
 WORKLOADS = {
@@ -53,10 +54,17 @@ WORKLOADS = {
         "deepseek_v3_blockwise", 4, (1, 128, 4096), 18432, 7168, "blockwise", "bf16", False,
         "DeepSeek-V3: A[M,7168] ~ Student-t(nu=4) for M in {1,128,4096}, "
         "W[18432,7168] ~ N(0,0.02^2); 1x128 activation groups, 128x128 weight blocks"),
+    "deepseek_v3_moe_grouped": Workload(
+        "deepseek_v3_moe_grouped", 5, (256, 4096), 4096, 7168, "grouped", "bf16", False,
+        "DeepSeek-V3 routed experts, gate and up projections fused (N = 2 x 2048), on one GPU "
+        "of eight-way expert parallelism (32 of 256 experts): M routed token rows in {256, "
+        "4096} ~ Student-t(nu=4), split over the experts by a multinomial draw with "
+        "Dirichlet(4) expert weights; each expert's W[4096,7168] ~ N(0,0.02^2) with its own "
+        "seed; 1x128 activation groups, 128x128 weight blocks", experts=32),
 }
 
 ORDER = ["pertensor_16x64x128", "tinyllama_upproj_prefill", "llama7b_decode",
-         "llama3_8b_mlp_blockwise", "deepseek_v3_blockwise"]
+         "llama3_8b_mlp_blockwise", "deepseek_v3_blockwise", "deepseek_v3_moe_grouped"]
 
 
 def to_bf16_bits(x):
@@ -103,9 +111,29 @@ def make_inputs(name, m=None):
     elif name == "deepseek_v3_blockwise":
         a = rng.standard_t(4.0, (mmax, K))
         b = 0.02 * rng.standard_normal((N, K), dtype=np.float32)
+    elif w.mode == "grouped":
+        # the routed rows; the expert weights come from expert_weight_bits, one expert at a time
+        return to_bf16_bits(rng.standard_t(4.0, (m, K)).astype(np.float32)), None
     else:
         raise KeyError(name)
     return to_bf16_bits(a[:m]), to_bf16_bits(b)
+
+
+def group_sizes(name, m):
+    """Rows per expert for a grouped workload with m routed rows: a multinomial draw of m over
+    the experts with Dirichlet(4) expert probabilities (imbalanced routing), seeded."""
+    w = WORKLOADS[name]
+    rng = np.random.default_rng([w.seed, m])
+    p = rng.dirichlet(np.full(w.experts, 4.0))
+    return rng.multinomial(m, p).astype(np.int64)
+
+
+def expert_weight_bits(name, e):
+    """Expert e's weight W_e [n, k] of a grouped workload, bf16 bit patterns, with its own
+    seed (so any subset of experts can be drawn alone)."""
+    w = WORKLOADS[name]
+    rng = np.random.default_rng([w.seed, 1000 + e])
+    return to_bf16_bits(0.02 * rng.standard_normal((w.n, w.k), dtype=np.float32))
 
 
 def bits_to_tensor(bits, dtype="bf16", device="cpu"):

@@ -162,3 +162,60 @@ def test_grouped_empty_and_validation():
     with pytest.raises(TypeError):
         fp8.fp8_gemm_grouped_blockwise(qa, torch.ones((0, 1), device=DEV), qb, torch.ones((2, 1, 1), device=DEV),
                                        off.to(torch.int64))
+
+
+# ----------------------------------------------------------------------------- workload
+
+MOE = "deepseek_v3_moe_grouped"
+_cache = {}
+
+
+def _expert_weights_on_gpu():
+    """Every expert's weight drawn on the host and quantized by the GPU (as the bench does)."""
+    if "gpu_w" not in _cache:
+        w = wl.WORKLOADS[MOE]
+        qb = torch.empty((w.experts, w.n, w.k), dtype=torch.uint8, device=DEV)
+        sb = torch.empty((w.experts, w.n // 128, w.k // 128), dtype=torch.float32, device=DEV)
+        for e in range(w.experts):
+            fp8.fp8_quantize_per_token_group(to_dev(wl.expert_weight_bits(MOE, e)), 128, 128, q=qb[e], scales=sb[e])
+        _cache["gpu_w"] = (qb, sb)
+    return _cache["gpu_w"]
+
+
+def _oracle_expert(e):
+    key = ("w", e)
+    if key not in _cache:
+        _cache[key] = oracle.quantize_groups(wl.expert_weight_bits(MOE, e), "bf16", 128, 128)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("m", [256, 4096])
+def test_moe_workload_sampled_experts(m):
+    """The MoE workload at full size in the bench's launch: all 32 experts' weights, the routed
+    rows quantized per token on the GPU, one grouped launch.  Three experts (the first, the
+    one with the most rows, the last) are checked in full: their weight codes and scales bit
+    for bit, and every output row routed to them within the product tolerance."""
+    w = wl.WORKLOADS[MOE]
+    a_bits, _ = wl.make_inputs(MOE, m)
+    sizes = wl.group_sizes(MOE, m)
+    off = oracle.offsets_from_sizes(sizes)
+    qb, sb = _expert_weights_on_gpu()
+    qa, sa = fp8.fp8_quantize_per_token_group(to_dev(a_bits), 1, 128)
+    d_off = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    c = fp8.fp8_gemm_grouped_blockwise(qa, sa, qb, sb, d_off)
+    got = out_to_f64(c)
+    qa_h, sa_h = host_u8(qa), host_f32(sa)
+    for e in sorted({0, int(np.argmax(sizes)), w.experts - 1}):
+        qb_e, sb_e = _oracle_expert(e)
+        assert_bytes_equal(host_u8(qb[e]), qb_e, f"expert {e} weight codes")
+        assert_bytes_equal(host_f32(sb[e]), sb_e, f"expert {e} weight scales")
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        qa_e, sa_e = oracle.quantize_groups(a_bits[lo:hi], "bf16", 1, 128)
+        assert_bytes_equal(qa_h[lo:hi], qa_e, f"expert {e} routed rows codes")
+        assert_bytes_equal(sa_h[lo:hi], sa_e, f"expert {e} routed rows scales")
+        one = np.array([0, hi - lo])
+        r = oracle.check_gemm(got[lo:hi], oracle.gemm_grouped_blockwise_ref(qa_e, sa_e, qb_e[None], sb_e[None], one),
+                              oracle.bound_grouped_blockwise(qa_e, sa_e, qb_e[None], sb_e[None], one), "bf16")
+        assert r["ok"], f"M={m} expert {e} ({hi - lo} rows): {r}"
