@@ -419,12 +419,13 @@ void launch_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* 
 }
 
 // Measured on MI355X with cold weights: one token runs best on the vector-ALU kernel
-// (1 KB row streams); from two tokens on the MFMA kernel, with two row blocks per wave once
-// the activation fragment is worth sharing (M > 4).
+// (1 KB row streams; one row per wave with four 1 KB loads in flight beat two or more rows
+// per wave by 5% at W[11008, 4096] and tied at W[18432, 7168]); from two tokens on the MFMA
+// kernel, with two row blocks per wave once the activation fragment is worth sharing (M > 4).
 template <int BW, int OUT>
 void launch_m(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
               int K, void* c, hipStream_t s) {
-  if (M == 1) launch_valu_t<BW, OUT, 1, 2, 4>(qa, sa, qb, sb, M, N, K, c, s);
+  if (M == 1) launch_valu_t<BW, OUT, 1, 1, 4>(qa, sa, qb, sb, M, N, K, c, s);
   else if (M <= 4) launch_t<BW, OUT, 2, 4, 1>(qa, sa, qb, sb, M, N, K, c, s);
   else launch_t<BW, OUT, 4, 2, 2>(qa, sa, qb, sb, M, N, K, c, s);
 }
