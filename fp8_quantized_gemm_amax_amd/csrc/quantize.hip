@@ -9,6 +9,12 @@
 // lane, 8-byte stores of eight codes.  For groups and blocks the amax, scale and cast are
 // fused in one pass that keeps the block's inputs in registers between the reduction and
 // the cast.
+//
+// Kernels: 1x128 groups and 128x128 blocks (float32 or UE8M0 scales); the whole tensor
+// (amax, then cast; one workgroup for small tensors); one scale per row (per output
+// channel or per token, the same page's per-channel scaling, section 5); the static cast
+// with a scale fixed in advance and the delayed-scaling update (the task page's
+// DelayedScaling recipe).
 #include "fp8_device.hpp"
 #include "launch.hpp"
 
