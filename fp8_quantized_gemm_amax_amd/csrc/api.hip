@@ -98,7 +98,7 @@ fp8_status_t fp8_amax(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
   if ((x && !aligned16(x)) || !aligned4(amax)) return FP8_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (whole) fp8amax::launch_tensor_reduce(static_cast<int>(dt), x, n, amax, false, s);
+  if (whole) fp8amax::launch_tensor_amax(static_cast<int>(dt), x, n, amax, s);
   else fp8amax::launch_groups(static_cast<int>(dt), x, rows, cols, block_rows, nullptr, amax, false, s);
   return finish_launch();
 }

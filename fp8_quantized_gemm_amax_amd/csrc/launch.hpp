@@ -35,21 +35,14 @@ void launch_groups_e8m0(int dt, const void* x, int64_t rows, int64_t cols, int32
 void launch_rows(int dt, const void* x, int64_t rows, int64_t cols, uint8_t* q, float* scales,
                  hipStream_t s);
 
-// Whole-tensor amax of n elements into the word `word`.  want_scale = false: the word ends
-// as the float amax.  want_scale = true: the word holds a pending reduction key that
-// launch_tensor_cast turns into the float scale amax / 448 (for n == 0 it is finished here).
-void launch_tensor_reduce(int dt, const void* x, int64_t n, float* word, bool want_scale,
-                          hipStream_t s);
+// Whole-tensor amax of n elements into the float *amax (0 for n == 0).
+void launch_tensor_amax(int dt, const void* x, int64_t n, float* amax, hipStream_t s);
 
-// Whole-tensor quantize of n elements: the scale word and the codes.  Small tensors take
-// one single-workgroup launch; larger ones launch_tensor_reduce + launch_tensor_cast.
+// Whole-tensor quantize of n > 0 elements: the scale and the codes.  Small tensors take one
+// single-workgroup launch; larger ones two launches, the first of which leaves partial
+// maxima in q that the second reads before it overwrites them with codes.
 void launch_tensor_quantize(int dt, const void* x, int64_t n, float* scale, uint8_t* q,
                             hipStream_t s);
-
-// q[i] = e4m3(x[i] / scale) for n > 0 elements, with the scale taken from (and written
-// back to) the word launch_tensor_reduce left.
-void launch_tensor_cast(int dt, const void* x, int64_t n, float* scale, uint8_t* q,
-                        hipStream_t s);
 
 // Static scaling: q[i] = e4m3(x[i] / *scale) for n > 0 elements in one pass; with amax_acc
 // the tensor's amax is folded into *amax_acc (float bits, atomic max).

@@ -86,8 +86,9 @@ fp8_status_t fp8_amax(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,
  *   x     : [rows, cols] of `dt`.
  *   q     : uint8 output [rows, cols], e4m3fn codes of x / scale.
  *   scale : float32 output [1], amax / 448 (1.0 for an all-zero or empty tensor).
- *           The same word also serves as the reduction's scratch while the call runs,
- *           so it must not alias x or q.
+ * Up to 32768 elements: one launch.  Above: two launches, the first of which leaves
+ * partial maxima in q that the second reads and then overwrites with the codes; so x and
+ * scale must not overlap q, and q holds no codes until the call has completed on `stream`.
  * Errors: as fp8_amax.
  */
 fp8_status_t fp8_quantize_per_tensor(const void* x, fp8_dtype_t dt, int64_t rows, int64_t cols,

@@ -184,25 +184,46 @@ def test_per_tensor_small_and_specials():
 
 @pytest.mark.parametrize("shape", [(1, 1), (3, 5), (1, 9), (1000, 1001), (2049, 3), (1, 8191), (1, 8192),
                                    (1, 10007), (257, 509), (1, 4096), (1, 32768), (128, 256), (181, 181),
-                                   (1, 32776), (1, 7168)])
+                                   (1, 32776), (1, 7168), (5, 8192), (4097, 1024), (3001, 3001)])
 def test_per_tensor_ragged(shape):
     """Ragged sizes on both per-tensor paths: up to 32768 elements one workgroup reduces,
-    scales and casts in one launch; beyond that three launches."""
+    scales and casts in one launch; beyond that two launches, the first leaving one partial
+    max per workgroup in every 8192-byte chunk of q.  5 x 8192 fills its chunks exactly;
+    4097 x 1024 has the most partials (128); 3001 x 3001 also the most chunks (1024), so the
+    cast workgroups loop over further chunks that hold no partials."""
     rng = np.random.default_rng(shape[0] + shape[1])
     check_tensor(wl.to_bf16_bits(rng.standard_normal(shape) * 3), "bf16", f"ragged {shape}")
 
 
-@pytest.mark.parametrize("rows", [300, 31])
+@pytest.mark.parametrize("rows", [300, 31, 9000])
 @pytest.mark.parametrize("where", ["first", "last", "tail"])
 def test_per_tensor_amax_position(where, rows):
     """The largest element at the very start, the very end and just before the end of a
-    tensor must each set the scale: every workgroup's share reaches the reduction (300
-    rows, three launches), and every wave's share in the one-workgroup path (31 rows)."""
+    tensor must each set the scale: every workgroup's partial reaches every cast workgroup
+    (300 and 9000 rows, two launches; 9000 rows has 128 partials and 1024 chunks), and every
+    wave's share in the one-workgroup path (31 rows)."""
     rng = np.random.default_rng(11)
     a = rng.standard_normal((rows, 1001))
     idx = {"first": (0, 0), "last": (rows - 1, 1000), "tail": (rows - 1, 990)}[where]
     a[idx] = -1000.0
     check_tensor(wl.to_bf16_bits(a), "bf16", f"amax at {where}")
+
+
+def test_per_tensor_reused_buffers():
+    """Two calls in a row into the same q and scale, the second on a smaller tensor with
+    fewer partials and chunks: the second call's scale comes from its own partials only,
+    though q still holds the first call's codes and partials."""
+    rng = np.random.default_rng(12)
+    big = wl.to_bf16_bits(rng.standard_normal((2000, 1000)) * 50)
+    small = wl.to_bf16_bits(rng.standard_normal((40, 1000)))
+    q = torch.empty(2000 * 1000, dtype=torch.uint8, device=DEV)
+    s = torch.empty(1, dtype=torch.float32, device=DEV)
+    for bits in (big, small):
+        n = bits.size
+        fp8.fp8_quantize_per_tensor(to_dev(bits, "bf16"), q=q[:n].view(bits.shape), scale=s)
+        q_want, s_want = oracle.quantize_per_tensor(bits, "bf16")
+        assert_bytes_equal(host_f32(s), np.array([s_want], np.float32), f"reused {bits.shape} scale")
+        assert_bytes_equal(host_u8(q[:n].view(bits.shape)), q_want, f"reused {bits.shape} codes")
 
 
 def test_per_tensor_empty():
