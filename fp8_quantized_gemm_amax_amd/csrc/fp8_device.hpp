@@ -18,16 +18,10 @@ enum : int { DT_BF16 = 0, DT_F16 = 1 };
 // = sa * sb with one scale per tensor; sa[m] * sb[n] with one scale per row of A (token)
 // and of B (output channel; the Transformer Engine page's per-channel scaling); `alpha`
 // = 1 in the slab-scaled modes, whose scales were applied inside the K loop.
-template <int SM>
-__device__ __forceinline__ float out_factor(float alpha, const float* sa, const float* sb, int m, int n) {
-  if constexpr (SM == SM_ROW) return sa[m] * sb[n];
-  else return alpha;
-}
-
-// The same factors for the fragment layout of the 16x16 MFMA outputs (lane l holds token
-// row 16 i + l % 16 and output columns 16 j + 4 (l / 16) + r), loaded when a kernel starts
-// so that the loads overlap its K loop instead of following it.  Rows and columns past
-// the ends read the last entry (their outputs are not stored).
+// For the fragment layout of the 16x16 MFMA outputs (lane l holds token row 16 i + l % 16
+// and output columns 16 j + 4 (l / 16) + r) the rowwise factors are loaded when a kernel
+// starts, so that the loads overlap its K loop instead of following it.  Rows and columns
+// past the ends read the last entry (their outputs are not stored).
 template <int SM, int MI, int NJ>
 struct FragFactors {
   static constexpr bool kRow = SM == SM_ROW;

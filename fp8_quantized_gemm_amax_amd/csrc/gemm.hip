@@ -164,6 +164,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
 
   // blockwise scales: sa for this lane's row in each M sub-tile, sb for the wave's block
   const int wave_n0 = n0 + wn * WN;
+  FragFactors<SM, TM, TN> ff;                        // rowwise epilogue scales, fetched now
+  ff.load(sa, sb, m0 + wm * WM, wave_n0, M, N);
   const int nb = wave_n0 / kSlab;
   const int NB = (N + kSlab - 1) / kSlab;
   auto load_scales = [&](int g, float* out, int* ea, int& eb) {
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       uint32_t h[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
+        h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * ff(alpha, i, j, r));
       if (vec_store && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
@@ -407,6 +409,10 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
 
   const int wave_n0 = n0 + wn * WN;
   const int nb = min(wave_n0, N - 1) / kSlab;
+  // rowwise epilogue factors, fetched now: loaded after the K loop, their latency was
+  // exposed load by load between the bf16 roundings (rowwise bf16 was 25% slower than fp16)
+  FragFactors<SM, TM, TN> ff;
+  ff.load(sa, sb, m0 + wm * WM, wave_n0, M, N);
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -483,7 +489,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
       uint32_t h[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * out_factor<SM>(alpha, sa, sb, m, min(n + r, N - 1)));
+        h[r] = f32_to_out_bits<OUT>(acc[i][j][r] * ff(alpha, i, j, r));
       if (vec_store && n + 3 < N) {
         *reinterpret_cast<uint2*>(crow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
