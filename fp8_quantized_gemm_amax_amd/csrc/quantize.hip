@@ -420,8 +420,9 @@ __global__ void finalize_word_kernel(uint32_t* word) {
 //    codes.
 // The slots cost P * B scattered 4-byte stores, written back as 32-byte pieces: at most
 // 1/10 of the pass's own traffic (128 x 128 of them, 0.5 MB, for 2^20 elements).
-// Measured against three launches (clear a word, atomic amax, cast) in HIP graphs: 0.55 us
-// less per step for A[512, 2048] and A[128, 4096].
+// Measured against three launches (clear a word, atomic amax, cast) in HIP graphs: 1.8 us
+// less per step for A[512, 2048] and 0.7 us for A[128, 4096]; 256-thread cast workgroups
+// (four times the slots) and fewer partial workgroups were slower.
 constexpr int kPartialThreads = 1024;
 constexpr int kCastThreads = 1024;
 constexpr int64_t kCastChunk = int64_t{kCastThreads} * 8;
