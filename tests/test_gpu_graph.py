@@ -1,6 +1,7 @@
 """The hot path captured in a HIP graph (as bench.py runs it) reproduces the eager
 results on every replay, with eager work and synchronisations between replays.  The
-per-tensor path clears its reduction word with a kernel, not a memset node."""
+per-tensor path clears nothing between calls: its partial maxima live in q, which is
+filled with junk before every replay here."""
 
 import numpy as np
 import pytest
