@@ -526,6 +526,10 @@ struct SkinnyShape {
   static constexpr int PER = IA + IS;
   static constexpr int A_BYTES = 16 * MB * kSlab;            // one stage of the A ring
   static constexpr int S_FLOATS = BLOCKWISE ? IS * 64 : 1;   // one stage of the scale ring
+  // float32 blockwise: the workgroup's whole activation-scale block (16 MB rows of K/128
+  // scales), staged once when it fits here (UE8M0 keeps the per-slab ring: staging its
+  // bytes as well made the grouped UE8M0 kernel spill registers)
+  static constexpr int PRE_BYTES = SM == SM_BLOCK ? 65536 : 16;
 };
 
 // The few-token product of one workgroup: A rows [0, M) (M <= 16 MB) times the 16 cw NB
@@ -536,7 +540,8 @@ template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
 __device__ __forceinline__ void skinny_body(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, int cw, uint16_t* __restrict__ c, int nblk,
-    uint8_t (*Abuf)[SkinnyShape<SM, MB>::A_BYTES], float (*Sbuf)[SkinnyShape<SM, MB>::S_FLOATS]) {
+    uint8_t (*Abuf)[SkinnyShape<SM, MB>::A_BYTES], float (*Sbuf)[SkinnyShape<SM, MB>::S_FLOATS],
+    uint8_t* Spre) {
   constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
@@ -552,6 +557,12 @@ __device__ __forceinline__ void skinny_body(
   const int nslabs = K / kSlab;                      // K % 128 == 0 on this path
   const int KG = nslabs;
   const int KG4 = static_cast<int>(e8m0_row_bytes(KG));   // UE8M0: bytes per scale row
+  // Activation scales of a slab lie 4 KG bytes apart, one cache line per token, so fetching
+  // them slab by slab costs as many L2 requests as the A slab itself.  From 64 tokens on,
+  // when the block fits, the loader stages it once (measured at 128 tokens, W[18432, 7168]:
+  // 53.7 -> 50.0 us); below that it gained nothing (MoE chunks of up to 17 tokens).
+  const int srow_bytes = 4 * KG;
+  const bool pre = SM == SM_BLOCK && M >= 64 && 16 * MB * srow_bytes <= SkinnyShape<SM, MB>::PRE_BYTES;
 
   if (w == cw) {
     // ---- loader wave ----
@@ -563,27 +574,48 @@ __device__ __forceinline__ void skinny_body(
     const int lc0 = (lane & 7) ^ (lane >> 4), lc1 = lc0 ^ 4;
     const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
     const uint32_t row_off = static_cast<uint32_t>((lane >> 3) * K);
-    auto issue = [&](int s, int st) {
+    auto issue = [&](int s, int st, bool scales) {
       const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
 #pragma unroll
       for (int j = 0; j < IA; ++j)
         dma16(ra, lds_addr(Abuf[st] + j * 1024),
               row_off + static_cast<uint32_t>(j * 8 * K) + k0 + ((j & 1) ? c_odd : c_even));
       if constexpr (BLOCKWISE) {
+        if (scales) {
 #pragma unroll
-        for (int j = 0; j < IS; ++j)
-          dma4(rs, lds_addr(Sbuf[st] + j * 64),
-               E8M0 ? static_cast<uint32_t>((j * 64 + lane) * KG4 + (s & ~3))
-                    : static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+          for (int j = 0; j < IS; ++j)
+            dma4(rs, lds_addr(Sbuf[st] + j * 64),
+                 E8M0 ? static_cast<uint32_t>((j * 64 + lane) * KG4 + (s & ~3))
+                      : static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+        }
       }
     };
+    if (pre) {
+      // the M scale rows in 256-byte pieces (scale pointers are only 4-byte aligned), at
+      // most 48 in flight.  Slab 0's wait covers them all.  Rows M .. 16 MB are not staged:
+      // their A rows are zero and their outputs are not stored.
+      const int pieces = (M * srow_bytes + 255) / 256;
+      for (int j = 0; j < pieces; ++j) {
+        if (j >= 48) wait_vmcnt<47>();
+        dma4(rs, lds_addr(Spre + j * 256), static_cast<uint32_t>(j * 256 + lane * 4));
+      }
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < nslabs) issue(p, p);
-    for (int s = 0; s < nslabs; ++s) {
-      wait_slabs_ahead<PER, NS - 2>(min(NS - 2, nslabs - 1 - s));
-      stage_barrier();
-      if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS);
+      for (int p = 0; p < NS - 1; ++p)
+        if (p < nslabs) issue(p, p, false);
+      for (int s = 0; s < nslabs; ++s) {
+        wait_slabs_ahead<IA, NS - 2>(min(NS - 2, nslabs - 1 - s));
+        stage_barrier();
+        if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS, false);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p)
+        if (p < nslabs) issue(p, p, true);
+      for (int s = 0; s < nslabs; ++s) {
+        wait_slabs_ahead<PER, NS - 2>(min(NS - 2, nslabs - 1 - s));
+        stage_barrier();
+        if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS, true);
+      }
     }
     return;
   }
@@ -649,7 +681,7 @@ __device__ __forceinline__ void skinny_body(
         ea = e8m0_byte(__float_as_uint(Sbuf[st][16 * b + r16]), s);
         eb = e8m0_byte(__float_as_uint(sbv[u]), s);
       } else if constexpr (BLOCKWISE) {
-        scl = Sbuf[st][16 * b + r16] * sbv[u];
+        scl = (pre ? reinterpret_cast<const float*>(Spre)[(16 * b + r16) * KG + s] : Sbuf[st][16 * b + r16]) * sbv[u];
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -728,7 +760,8 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_skinny_kernel(
   using Shape = SkinnyShape<SM, MB>;
   __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][Shape::A_BYTES];
   __shared__ __attribute__((aligned(16))) float Sbuf[NS][Shape::S_FLOATS];
-  skinny_body<SM, OUT, NB, MB, NS, UNROLL>(qa, sa, qb, sb, M, N, K, cw, c, blockIdx.x, Abuf, Sbuf);
+  __shared__ __attribute__((aligned(16))) uint8_t Spre[Shape::PRE_BYTES];
+  skinny_body<SM, OUT, NB, MB, NS, UNROLL>(qa, sa, qb, sb, M, N, K, cw, c, blockIdx.x, Abuf, Sbuf, Spre);
 }
 
 // Grouped (mixture-of-experts) product: expert e's tokens are the rows
@@ -749,6 +782,7 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_grouped_kernel(
   using Shape = SkinnyShape<SM, MB>;
   __shared__ __attribute__((aligned(1024))) uint8_t Abuf[NS][Shape::A_BYTES];
   __shared__ __attribute__((aligned(16))) float Sbuf[NS][Shape::S_FLOATS];
+  __shared__ __attribute__((aligned(16))) uint8_t Spre[Shape::PRE_BYTES];
   __shared__ int tile[3];                           // expert (-1: none), first row, rows
   constexpr int CH = 16 * MB;
   if (threadIdx.x < 64) {
@@ -799,7 +833,7 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_grouped_kernel(
   skinny_body<SM, OUT, NB, MB, NS, UNROLL>(
       qa + static_cast<int64_t>(row0) * K, static_cast<const uint8_t*>(sa) + row0 * sa_row,
       qb + static_cast<int64_t>(e) * N * K, static_cast<const uint8_t*>(sb) + e * sb_rows * sa_row,
-      rows, N, K, cw, c + static_cast<int64_t>(row0) * N, blockIdx.x % nblks, Abuf, Sbuf);
+      rows, N, K, cw, c + static_cast<int64_t>(row0) * N, blockIdx.x % nblks, Abuf, Sbuf, Spre);
 }
 
 template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>

@@ -170,6 +170,18 @@ def test_few_token_regime_shapes(mode, M, N, K):
     assert_close(got, c64, bnd, "bf16", f"{mode} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,K", [(128, 16384), (100, 16512), (64, 32768), (64, 32896), (32, 65536), (20, 65664)])
+def test_few_token_scale_block_staging(M, K):
+    """Float32 activation scales of the few-token kernel are staged into LDS once per
+    workgroup from 64 tokens on while its block (16 MB rows x K/128 scales) fits in 64 KB,
+    and fetched slab by slab otherwise: both sides of that limit for tiles of 128 and 64
+    token rows, and 32-row tiles (always slab by slab)."""
+    qa, sa, qb, sb = random_case("blockwise", M, 300, K, M + K)
+    got = run_gemm("blockwise", qa, sa, qb, sb, "bf16")
+    c64, bnd = reference("blockwise", qa, sa, qb, sb)
+    assert_close(got, c64, bnd, "bf16", f"blockwise {M}x300x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 64, 256), (1, 70, 1040), (5, 70, 256), (3, 33, 2064), (128, 300, 256),
                                    (20, 70, 384)])
 def test_one_hot_layout(M, N, K):

@@ -91,6 +91,17 @@ def test_grouped_matches_oracle(sizes, N, K, out_dtype, ue8m0):
     check(got, qa, sa, qb, sb, off, out_dtype, f"{sizes} N={N} K={K}", ue8m0)
 
 
+@pytest.mark.parametrize("K", [16384, 16512])
+def test_grouped_scale_block_staging(K):
+    """The grouped launch stages a chunk's float32 activation scales into LDS when it has at
+    least 64 tokens and 128 rows x K/128 scales fit in 64 KB: at K = 16384 the chunks of 128
+    and 72 tokens stage them and the 56-token chunk takes them slab by slab; at K = 16512
+    every chunk does."""
+    qa, sa, qb, sb, off = grouped_case([200, 0, 56], 130, K, K)
+    got = run_grouped(qa, sa, qb, sb, off, "bf16")
+    check(got, qa, sa, qb, sb, off, "bf16", f"staging K={K}")
+
+
 def test_grouped_many_experts():
     """96 experts with sizes 0..40 (a third of them empty): the tile search crosses two
     64-expert batches."""
