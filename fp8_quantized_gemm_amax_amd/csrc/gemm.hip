@@ -526,10 +526,9 @@ struct SkinnyShape {
   static constexpr int PER = IA + IS;
   static constexpr int A_BYTES = 16 * MB * kSlab;            // one stage of the A ring
   static constexpr int S_FLOATS = BLOCKWISE ? IS * 64 : 1;   // one stage of the scale ring
-  // float32 blockwise: the workgroup's whole activation-scale block (16 MB rows of K/128
-  // scales), staged once when it fits here (UE8M0 keeps the per-slab ring: staging its
-  // bytes as well made the grouped UE8M0 kernel spill registers)
-  static constexpr int PRE_BYTES = SM == SM_BLOCK ? 65536 : 16;
+  // blockwise: the workgroup's whole activation-scale block (16 MB rows of K/128 float32
+  // scales, or of padded UE8M0 byte rows), staged once when it fits here
+  static constexpr int PRE_BYTES = BLOCKWISE ? 65536 : 16;
 };
 
 // The few-token product of one workgroup: A rows [0, M) (M <= 16 MB) times the 16 cw NB
@@ -557,12 +556,15 @@ __device__ __forceinline__ void skinny_body(
   const int nslabs = K / kSlab;                      // K % 128 == 0 on this path
   const int KG = nslabs;
   const int KG4 = static_cast<int>(e8m0_row_bytes(KG));   // UE8M0: bytes per scale row
-  // Activation scales of a slab lie 4 KG bytes apart, one cache line per token, so fetching
+  // Activation scales of a slab lie a scale row apart, one cache line per token, so fetching
   // them slab by slab costs as many L2 requests as the A slab itself.  From 64 tokens on,
   // when the block fits, the loader stages it once (measured at 128 tokens, W[18432, 7168]:
-  // 53.7 -> 50.0 us); below that it gained nothing (MoE chunks of up to 17 tokens).
-  const int srow_bytes = 4 * KG;
-  const bool pre = SM == SM_BLOCK && M >= 64 && 16 * MB * srow_bytes <= SkinnyShape<SM, MB>::PRE_BYTES;
+  // 53.7 -> 50.0 us); below that it gained nothing (MoE chunks of up to 17 tokens).  UE8M0
+  // stages only with one weight fragment per wave: with two (the grouped launch) the
+  // staged path made the kernel spill registers.
+  const int srow_bytes = E8M0 ? KG4 : 4 * KG;
+  constexpr bool kCanStage = SM == SM_BLOCK || (E8M0 && NB == 1);
+  const bool pre = kCanStage && M >= 64 && 16 * MB * srow_bytes <= SkinnyShape<SM, MB>::PRE_BYTES;
 
   if (w == cw) {
     // ---- loader wave ----
@@ -678,7 +680,8 @@ __device__ __forceinline__ void skinny_body(
       float scl = 0.0f;
       int ea = 127, eb = 127;
       if constexpr (E8M0) {
-        ea = e8m0_byte(__float_as_uint(Sbuf[st][16 * b + r16]), s);
+        ea = pre ? static_cast<int>(Spre[(16 * b + r16) * KG4 + s])
+                 : e8m0_byte(__float_as_uint(Sbuf[st][16 * b + r16]), s);
         eb = e8m0_byte(__float_as_uint(sbv[u]), s);
       } else if constexpr (BLOCKWISE) {
         scl = (pre ? reinterpret_cast<const float*>(Spre)[(16 * b + r16) * KG + s] : Sbuf[st][16 * b + r16]) * sbv[u];

@@ -125,6 +125,16 @@ def test_shapes(M, N, K, out_dtype):
     check(run_gemm(qa, ea, qb, eb, out_dtype), qa, ea, qb, eb, out_dtype, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(128, 130, 8192), (128, 130, 65536), (100, 130, 65664), (64, 40, 131072),
+                                   (64, 40, 131200)])
+def test_few_token_scale_block_staging(M, N, K):
+    """The few-token kernel stages a workgroup's UE8M0 activation-scale rows into LDS from 64
+    tokens on while 16 MB rows of padded scale bytes fit in 64 KB, and takes them slab by
+    slab past that: both sides of the limit for 128- and 64-row tiles."""
+    qa, ea, qb, eb = random_case(M, N, K, M + K)
+    check(run_gemm(qa, ea, qb, eb, "bf16"), qa, ea, qb, eb, "bf16", f"staging {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(2050, 8200, 256), (1030, 4100, 384), (520, 33000, 128)])
 def test_large_tile_paths(M, N, K):
     """The 256x256 tile (at least one tile per CU) and the four-wave 128x128 tile."""
