@@ -107,6 +107,53 @@ def _need_cuda(*ts):
             raise ValueError("all tensors must be on the GPU")
 
 
+def _same_device(like, *ts):
+    """Every tensor on like's GPU (the library launches on like's stream)."""
+    _need_cuda(like, *ts)
+    for t in ts:
+        if t is not None and t.device != like.device:
+            raise ValueError(f"all tensors must be on {like.device}, got one on {t.device}")
+
+
+def _span(t):
+    """[first, last) byte addresses a contiguous tensor covers."""
+    lo = t.data_ptr()
+    return lo, lo + t.numel() * t.element_size()
+
+
+def _overlaps(a, b):
+    if a is None or b is None or a.numel() == 0 or b.numel() == 0:
+        return False
+    (a0, a1), (b0, b1) = _span(a), _span(b)
+    return a0 < b1 and b0 < a1
+
+
+def _check_out(t, shape, dtypes, what, like, inputs=()):
+    """A caller-supplied output buffer: on like's device, contiguous, one of `dtypes`, exactly
+    `shape`, and sharing no memory with any of `inputs`.  Checked before any library call:
+    the kernels write the full extent of an output, so a smaller or strided buffer would be
+    written past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    for x in inputs:
+        if _overlaps(t, x):
+            raise ValueError(f"{what} overlaps an input")
+    _same_device(like, t)
+    return t
+
+
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+_F32 = (torch.float32,)
+_U8 = (torch.uint8,)
+_OUT = (torch.bfloat16, torch.float16)
+
+
 def _as_2d(x):
     if x.dim() != 2:
         raise ValueError(f"expected a 2-D tensor, got shape {tuple(x.shape)}")
@@ -131,7 +178,7 @@ def fp8_amax(x, block_rows=0, block_cols=0, out=None):
         -(-R // max(block_rows, 1)), -(-C // max(block_cols, 1)))
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
-    _need_cuda(out)
+    _check_out(out, shape, _F32, "out", x, (x,))
     _check("fp8_amax", lib().fp8_amax(_ptr(x), _dt(x), R, C, block_rows, block_cols,
                                       ctypes.c_void_p(out.data_ptr()), _stream(x)))
     return out
@@ -146,7 +193,10 @@ def fp8_quantize_per_tensor(x, q=None, scale=None):
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty((1,), dtype=torch.float32, device=x.device)
-    _need_cuda(q, scale)
+    # q also holds the partial maxima between the call's two launches: it must not share
+    # memory with x, which the second launch reads again
+    _check_out(q, (R, C), _CODES, "q", x, (x,))
+    _check_out(scale, (1,), _F32, "scale", x, (x, q))
     _check("fp8_quantize_per_tensor",
            lib().fp8_quantize_per_tensor(_ptr(x), _dt(x), R, C, _ptr(q),
                                          ctypes.c_void_p(scale.data_ptr()), _stream(x)))
@@ -160,10 +210,11 @@ def fp8_quantize_per_token_group(x, group_rows=1, group_cols=128, q=None, scales
     R, C = x.shape
     if q is None:
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    grid = (-(-R // max(group_rows, 1)), -(-C // max(group_cols, 1)))
     if scales is None:
-        scales = torch.empty((-(-R // max(group_rows, 1)), -(-C // max(group_cols, 1))),
-                             dtype=torch.float32, device=x.device)
-    _need_cuda(q, scales)
+        scales = torch.empty(grid, dtype=torch.float32, device=x.device)
+    _check_out(q, (R, C), _CODES, "q", x, (x,))
+    _check_out(scales, grid, _F32, "scales", x, (x, q))
     _check("fp8_quantize_per_token_group",
            lib().fp8_quantize_per_token_group(_ptr(x), _dt(x), R, C, group_rows, group_cols,
                                               _ptr(q), _ptr(scales), _stream(x)))
@@ -180,9 +231,8 @@ def fp8_quantize_rowwise(x, q=None, scales=None):
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((R,), dtype=torch.float32, device=x.device)
-    _need_cuda(q, scales)
-    if scales.numel() != R:
-        raise ValueError(f"rowwise scales must have {R} entries, got {scales.numel()}")
+    _check_out(q, (R, C), _CODES, "q", x, (x,))
+    _check_out(scales, (R,), _F32, "scales", x, (x, q))
     _check("fp8_quantize_rowwise",
            lib().fp8_quantize_rowwise(_ptr(x), _dt(x), R, C, _ptr(q), _ptr(scales), _stream(x)))
     return q, scales
@@ -202,10 +252,11 @@ def fp8_quantize_per_token_group_ue8m0(x, group_rows=1, group_cols=128, q=None, 
     R, C = x.shape
     if q is None:
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    grid = (-(-R // max(group_rows, 1)), e8m0_row_bytes(-(-C // max(group_cols, 1))))
     if scales is None:
-        scales = torch.empty((-(-R // max(group_rows, 1)), e8m0_row_bytes(-(-C // max(group_cols, 1)))),
-                             dtype=torch.uint8, device=x.device)
-    _need_cuda(q, scales)
+        scales = torch.empty(grid, dtype=torch.uint8, device=x.device)
+    _check_out(q, (R, C), _CODES, "q", x, (x,))
+    _check_out(scales, grid, _U8, "scales", x, (x, q))
     _check("fp8_quantize_per_token_group_ue8m0",
            lib().fp8_quantize_per_token_group_ue8m0(_ptr(x), _dt(x), R, C, group_rows, group_cols,
                                                     _ptr(q), _ptr(scales), _stream(x)))
@@ -214,7 +265,7 @@ def fp8_quantize_per_token_group_ue8m0(x, group_rows=1, group_cols=128, q=None, 
 
 def _gemm(name, qa, sa, qb, sb, out_dtype, out, scale_dtype=torch.float32):
     qa, qb = _codes(_as_2d(qa)), _codes(_as_2d(qb))
-    _need_cuda(qa, qb, sa, sb)
+    _same_device(qa, qb, sa, sb)
     M, K = qa.shape
     N, K2 = qb.shape
     if K != K2:
@@ -225,7 +276,7 @@ def _gemm(name, qa, sa, qb, sb, out_dtype, out, scale_dtype=torch.float32):
         raise TypeError(f"scales must be {scale_dtype}")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
-    _need_cuda(out)
+    _check_out(out, (M, N), _OUT, "out", qa, (qa, qb, sa, sb))
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, _ptr(out), _out_dt(out.dtype),
                     _stream(qa)))
@@ -254,7 +305,7 @@ def _grouped(name, qa, sa, qb, sb, offsets, out_dtype, out, scale_dtype):
     if qb.dim() != 3:
         raise ValueError(f"expert weights must be [E, N, K], got {tuple(qb.shape)}")
     qb = qb.contiguous()
-    _need_cuda(qa, qb, sa, sb, offsets)
+    _same_device(qa, qb, sa, sb, offsets)
     T, K = qa.shape
     E, N, K2 = qb.shape
     if K != K2:
@@ -271,7 +322,7 @@ def _grouped(name, qa, sa, qb, sb, offsets, out_dtype, out, scale_dtype):
                              f"got {tuple(sa.shape)} and {tuple(sb.shape)}")
     if out is None:
         out = torch.empty((T, N), dtype=out_dtype, device=qa.device)
-    _need_cuda(out)
+    _check_out(out, (T, N), _OUT, "out", qa, (qa, qb, sa, sb, offsets))
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(offsets), E, T, N, K, _ptr(out),
                     _out_dt(out.dtype), _stream(qa)))
@@ -325,10 +376,11 @@ def fp8_quantize_static(x, scale, q=None, amax_acc=None):
     R, C = x.shape
     if q is None:
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
-    _need_cuda(q)
+    _same_device(x, scale)
+    _check_out(q, (R, C), _CODES, "q", x, (x, scale))
     acc = None
     if amax_acc is not None:
-        _need_cuda(amax_acc)
+        _same_device(x, amax_acc)
         if amax_acc.element_size() != 4 or amax_acc.numel() != 1:
             raise TypeError("amax_acc must be one 32-bit word on the device")
         acc = ctypes.c_void_p(amax_acc.data_ptr())
@@ -394,7 +446,8 @@ def fp8_quantize_delayed(x, history, amax_acc, step, interval, margin, scale, sc
     R, C = x.shape
     if q is None:
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
-    _need_cuda(q)
+    _same_device(x, history, amax_acc, step, scale, scale_used)
+    _check_out(q, (R, C), _CODES, "q", x, (x, history, amax_acc, step, scale, scale_used))
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
     _check("fp8_quantize_delayed",
            lib().fp8_quantize_delayed(_ptr(x), _dt(x), R, C, vp(history), history.numel(), vp(amax_acc),
@@ -411,5 +464,6 @@ def fp8_debug_cast_f32(v, q=None):
         raise TypeError("fp8_debug_cast_f32 takes float32")
     if q is None:
         q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check_out(q, v.shape, _CODES, "q", v, (v,))
     _check("fp8_debug_cast_f32", lib().fp8_debug_cast_f32(_ptr(v), _ptr(q), v.numel(), _stream(v)))
     return q

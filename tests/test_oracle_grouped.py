@@ -94,3 +94,38 @@ def test_offsets_must_cover_the_rows():
         gemm_grouped_blockwise_ref(qa, sa, qb, sb, np.array([0, 2, 3]))
     with pytest.raises(AssertionError):
         gemm_grouped_blockwise_ref(qa, sa, qb, sb, np.array([0, 3, 2]))
+
+
+def test_ue8m0_grouped_bound_exact_and_decoded():
+    """bound_grouped_blockwise_ue8m0 is the magnitude term of the grouped UE8M0 tolerance.
+    Pinned three ways: it equals the float-scale grouped bound with the bytes decoded to
+    2^(c - 127); a few entries equal an exact rational sum over k of
+    |dec(qa)·2^(ea-127)|·|dec(qb)·2^(eb-127)| with the row's expert found by searching the
+    offsets (taking the scale bytes as plain numbers instead would miss by a factor of about
+    127^2 and fail here); and it is at least |C| everywhere, with equality where every
+    product of a row and column has one sign."""
+    from oracle.grouped import bound_grouped_blockwise_ue8m0
+    rng = np.random.default_rng(7)
+    sizes = [3, 0, 4]
+    T, N, K = 7, 140, 256
+    qa, qb = rng.choice(FINITE, (T, K)), rng.choice(FINITE, (3, N, K))
+    ea = rng.integers(112, 142, (T, 2)).astype(np.uint8)
+    eb = rng.integers(112, 142, (3, 2, 2)).astype(np.uint8)
+    off = offsets_from_sizes(sizes)
+    got = bound_grouped_blockwise_ue8m0(qa, ea, qb, eb, off)
+    dec = lambda e: np.exp2(e.astype(np.float64) - 127).astype(np.float32)
+    np.testing.assert_array_equal(got, bound_grouped_blockwise(qa, dec(ea), qb, dec(eb), off))
+    da, db = oracle.decode_e4m3(qa), oracle.decode_e4m3(qb)
+    for t in (0, 2, 3, 6):
+        e = int(np.searchsorted(off, t, side="right") - 1)
+        for n in (0, 127, 128, 139):
+            mag = sum(abs(Fraction(float(da[t, k])) * Fraction(2) ** (int(ea[t, k // 128]) - 127) *
+                          Fraction(float(db[e, n, k])) * Fraction(2) ** (int(eb[e, n // 128, k // 128]) - 127))
+                      for k in range(K))
+            assert abs(Fraction(float(got[t, n])) - mag) <= mag * Fraction(1, 2 ** 50), (t, n)
+    c = gemm_grouped_blockwise_ue8m0_ref(qa, ea, qb, eb, off)
+    assert np.all(got >= np.abs(c))
+    # one sign everywhere: the bound equals |C|
+    qa1, qb1 = qa & 0x7F, qb & 0x7F
+    np.testing.assert_allclose(bound_grouped_blockwise_ue8m0(qa1, ea, qb1, eb, off),
+                               np.abs(gemm_grouped_blockwise_ue8m0_ref(qa1, ea, qb1, eb, off)), rtol=1e-14)
