@@ -11,9 +11,12 @@ rotation whose footprint exceeds 1 GiB, so reads come from HBM rather than the 2
 Infinity Cache.
 
 Prints one JSON line.  `value` is the whole step's throughput (TFLOP/s including the
-activation quantize; GB/s for M <= 16 decode), `roofline` rates the dominant kernel
-(the GEMM) from HIP events around each of its launches in the timed region, and
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+activation quantize; GB/s for M <= 16 decode) from HIP events around the graph replays of
+the timed region (mean, with the median and 10th/90th percentiles over replays);
+`roofline` rates the dominant kernel (the GEMM) from HIP events around each of its
+launches in a step-by-step pass where every GEMM follows its own quantize, as in the
+timed steps; `cpu_baseline` times the CPU oracle on a bounded sample of the same workload;
+`machine` records the GPU's compute units and clock, the ROCm version and the host CPU.
 """
 
 import argparse
@@ -29,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "FP8 scaled-GEMM TFLOP/s incl. quantize (% MFMA FP8 peak); decode GB/s (% HBM)"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, 8 TB/s
-DEFAULT_WORKLOAD = "tinyllama_upproj_prefill"
+DEFAULT_WORKLOAD = "deepseek_v3_blockwise"   # the largest configuration: M=4096, N=18432, K=7168
 ROTATION_BYTES = 1 << 30
 DELAYED_HISTORY = 16          # amax history length of the delayed recipe (the pages give none)
 DELAYED_INTERVAL = 4          # the recipe's interval and margin
@@ -105,6 +108,41 @@ def measured_traffic(workload, M, scheme="tensorwise"):
     if not e or e.get("kernel_source_sha") != kernel_source_hash():
         return None
     return e.get("traffic_bytes_per_launch")
+
+
+def machine_facts():
+    """Compute units and clocks of GPU 0, the ROCm and HIP versions, the host CPU model."""
+    import subprocess
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    facts = {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+             "compute_units": props.multi_processor_count, "hip": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            facts["rocm"] = f.read().strip()
+    except OSError:
+        facts["rocm"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            facts["host_cpu"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        facts["host_cpu"] = None
+    facts["host_threads"] = len(os.sched_getaffinity(0))
+    try:                         # current and highest shader clock levels (MHz)
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        facts["sclk"] = card.get("sclk clock speed:") or card.get("sclk clock level:")
+    except Exception:            # tool missing or output changed: leave the clock unrecorded
+        facts["sclk"] = None
+    return facts
+
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 6), "p10": round(float(np.percentile(a, 10)), 6),
+            "p90": round(float(np.percentile(a, 90)), 6), "n": int(a.size)}
 
 
 def copy_reference(mib, steps):
@@ -187,7 +225,7 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
         qb, sb = oracle.quantize_groups_ue8m0(b_bits, "bf16", 128, 128)
     else:
         qb, sb = oracle.quantize_groups(b_bits, "bf16", 128, 128)
-    rows = M
+    rows = min(M, 64)          # a first timing on a few rows sizes the sample
     runs = []
     t_start = time.perf_counter()
     while True:
@@ -217,8 +255,8 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
             oracle.gemm_blockwise_ref(qa, sa, qb, sb)
         dt = time.perf_counter() - t0
         runs.append(dt)
-        if dt * 3 > budget_s and rows > 1 and len(runs) == 1:
-            rows = max(1, int(rows * budget_s / (3 * dt)))
+        if len(runs) == 1 and (dt * 3 > budget_s and rows > 1 or dt * 3 < 0.5 * budget_s and rows < M):
+            rows = max(1, min(M, int(rows * budget_s / (3 * max(dt, 1e-6)))))
             runs = []
             continue
         if len(runs) >= 3 or time.perf_counter() - t_start > budget_s:
@@ -417,51 +455,67 @@ def main():
     ref_c = sets[0]["c"].clone()
 
     # HIP graphs: one replay runs `R` steps (one per rotation set); a tail graph runs the
-    # remaining K mod R, so exactly K steps are timed.  A second graph holds the R GEMMs
-    # alone; its replays time the dominant kernel.
+    # remaining K mod R, so exactly K steps are timed.  Every graph is replayed once before
+    # the timed region.
     K_steps = args.steps
-    def capture(n, fn):
+    def capture(n, fn, first=0):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(n):
+            for i in range(first, first + n):
                 fn(sets[i % R])
         return g
     n_full, tail = divmod(K_steps, R)
     g_full = capture(R, step) if n_full else None
     g_tail = capture(tail, step) if tail else None
-    g_gemm = capture(R, gemm)
     for _ in range(2):                      # graph warm-up replays
-        if g_full:
-            g_full.replay()
-        g_gemm.replay()
+        for g in (g_full, g_tail):
+            if g is not None:
+                g.replay()
     torch.cuda.synchronize()
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: an event pair around every replay; the per-step time of a replay is its
+    # duration over the steps it holds
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_full + (1 if tail else 0))]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(n_full):
+    for i in range(n_full):
+        ev[i][0].record()
         g_full.replay()
+        ev[i][1].record()
     if g_tail:
+        ev[-1][0].record()
         g_tail.replay()
-    end.record()
+        ev[-1][1].record()
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
+    sizes_ = [R] * n_full + ([tail] if tail else [])
+    durs = [a.elapsed_time(b) for a, b in ev]
+    total_ms = ev[0][0].elapsed_time(ev[-1][1])
     ms_per_step = total_ms / K_steps
+    step_dist = percentiles([d / n for d, n in zip(durs, sizes_)])
 
     # the same steps replayed must reproduce the eager output bit for bit
     if not torch.equal(sets[0]["c"].view(torch.int16), ref_c.view(torch.int16)):
         raise RuntimeError("graph replay output differs from the eager step")
 
-    gemm_reps = max(1, -(-K_steps // R))
-    gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gs.record()
-    for _ in range(gemm_reps):
-        g_gemm.replay()
-    ge.record()
+    # the GEMM's time per launch: the same steps without their GEMMs (a graph of the R
+    # quantizes, replayed as often as the step graph) are timed with events on the same
+    # stream, and their time per step is taken off the step's.  Every GEMM thus runs right
+    # after its own quantize, as in the timed steps, and no launch gap or event sits between
+    # a GEMM and the next kernel.
+    g_q = capture(R, quantize)
+    g_q.replay()
     torch.cuda.synchronize()
-    gemm_ms = gs.elapsed_time(ge) / (gemm_reps * R)
+    reps = max(1, -(-K_steps // R))
+    qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in qev:
+        a.record()
+        g_q.replay()
+        b.record()
+    torch.cuda.synchronize()
+    quant_ms = sum(a.elapsed_time(b) for a, b in qev) / (reps * R)
+    gemm_ms = ms_per_step - quant_ms
 
     flops = 2.0 * M * N * K
     step_bytes, gemm_bytes = algorithmic_bytes(w, M, scheme)
@@ -493,8 +547,9 @@ def main():
                    "scale_fmt": args.scale_fmt if (blockwise or grouped) else "float32",
                    "act_scaling": args.act_scaling if not blockwise else "dynamic",
                    "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
-                   "gemm_ms": round(gemm_ms, 6), "host_s": round(host_s, 4),
+                   "gemm_ms": round(gemm_ms, 6), "quantize_ms": round(quant_ms, 6), "host_s": round(host_s, 4),
                    "step_bytes": step_bytes},
+        "step_ms": step_dist,
         "roofline": roof,
     }
     if delayed:
@@ -503,6 +558,7 @@ def main():
     if grouped:
         result["config"].update({"experts": w.experts, "rows_per_expert_min": int(sizes.min()),
                                  "rows_per_expert_max": int(sizes.max())})
+    result["machine"] = machine_facts()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scheme=scheme)
     print(json.dumps(result), flush=True)

@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -16,9 +17,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp8amax.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemv.hip"]
+OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # exact IEEE float32 arithmetic in the quantizer: no contraction, no fast math
     "-ffp-contract=off",
     # no packed fp32 (v_pk_*_f32) instructions in device code
@@ -37,17 +39,27 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libfp8amax.so)")
 
 
-def build_library(verbose=False):
-    """Compile every HIP source into LIB_PATH.  Always recompiles."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[-3:])}")
+
+
+def build_library(verbose=False):
+    """Compile every HIP source to an object (in parallel), then link LIB_PATH.  Always
+    recompiles."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    cmds = [[hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, os.path.join(CSRC, src)]
+            for src, obj in zip(SOURCES, objs)]
+    workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as pool:
+        list(pool.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

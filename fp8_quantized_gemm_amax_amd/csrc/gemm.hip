@@ -32,48 +32,16 @@
 
 #include "dma.hpp"
 #include "fp8_device.hpp"
+#include "gemm_common.hpp"
 #include "launch.hpp"
 
 namespace fp8amax {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+using namespace gemm;
 
-constexpr int kThreads = 256;
-constexpr int kSlab = 128;
-constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past any range: the load returns zeros
-
-// 16-byte chunk swizzle of LDS slab rows (see the layout note above)
-__host__ __device__ constexpr int swz(int row) { return (row >> 1) & 7; }
-
-__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
-  // cbsz = blgp = 0: both operands e4m3; E8M0 scale 127 = 2^0 on both.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
-// The same product with E8M0 block scales: each lane's 32 K positions of the first operand
-// are scaled by 2^(ea - 127) and those of the second by 2^(eb - 127) (measured on gfx950:
-// a lane's scale byte covers exactly the 32 K positions it holds, for both operands).
-__device__ __forceinline__ v4f mfma_fp8_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                     // nearest even
-}
-
-template <int OUT>
-__device__ __forceinline__ uint32_t f32_to_out_bits(float f) {
-  if constexpr (OUT == DT_BF16) {
-    return f32_to_bf16_bits(f);
-  } else {
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
-  }
-}
+constexpr int kThreads = 256;      // the register-staged kernel
 
 template <int BM, int BN, int WM, int WN, int SM, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
@@ -283,23 +251,6 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
 // Tile order: workgroup b runs on XCD b % 8; consecutive tiles of a grouped order
 // (groups of kGroupM tile rows) are given to the same XCD so its L2 serves their shared
 // A rows and B columns.
-constexpr int kGroupM = 8;
-constexpr int kXcds = 8;
-
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  const int q = total / kXcds, r = total % kXcds;
-  const int x = b % kXcds, i = b / kXcds;
-  const int logical = x * q + min(x, r) + i;
-  const int per_group = kGroupM * tiles_n;
-  const int g = logical / per_group;
-  const int first_m = g * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_g = logical - g * per_group;
-  tm = first_m + in_g % gsize;
-  tn = in_g / gsize;
-}
-
 // Wait until at most `ahead` slabs of PER vector-memory operations each are still in flight
 // (A = the most the pipeline ever leaves outstanding).
 template <int PER, int A>
@@ -318,11 +269,11 @@ __device__ __forceinline__ void wait_slabs_ahead(int ahead) {
 template <int BM, int BN, int WM, int WN>
 constexpr int dma_threads() { return 64 * (BM / WM) * (BN / WN); }
 
-template <int BM, int BN, int WM, int WN, int SM, int OUT, int NS>
+template <int BM, int BN, int WM, int WN, int SM, int OUT, int NS, bool PAIR = false>
 __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kernel(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
     const void* __restrict__ sb_, int M, int N, int K, uint16_t* __restrict__ c, int tiles_m,
-    int tiles_n) {
+    int tiles_n, int ldc) {
   constexpr bool BLOCKWISE = slab_scaled(SM);
   constexpr bool E8M0 = SM == SM_E8M0;
   const float* __restrict__ sa = static_cast<const float*>(sa_);
@@ -376,9 +327,48 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     rs = make_rsrc(sa + static_cast<int64_t>(srow0) * KG,
                    static_cast<uint32_t>(max(0, min(WM, M - srow0)) * KG * 4));
 
+  // PAIR (eight waves): waves w and w + 4 share a SIMD; the first of the pair issues the
+  // slab's DMA for both, so the second keeps the SIMD's matrix unit busy while the first
+  // waits for room in the memory queue
+  static_assert(!PAIR || WAVES == 8, "pairs of waves on one SIMD");
+  const bool lead = !PAIR || w < 4;
+  const int wp = PAIR ? w + 4 : w;                         // the partner's wave index
+  const int srow0p = m0 + (wp / WAVES_N) * WM;
+  v4i rsp = {0, 0, 0, 0};
+  if constexpr (PAIR && E8M0)
+    rsp = make_rsrc(static_cast<const uint8_t*>(sa_) + static_cast<int64_t>(srow0p) * KG4,
+                    static_cast<uint32_t>(max(0, min(WM, M - srow0p)) * KG4));
+  else if constexpr (PAIR && BLOCKWISE)
+    rsp = make_rsrc(sa + static_cast<int64_t>(srow0p) * KG,
+                    static_cast<uint32_t>(max(0, min(WM, M - srow0p)) * KG * 4));
+  const uint32_t row_off_p = static_cast<uint32_t>(((wp * IA) * 8 + (lane >> 3)) * K);
+  const uint32_t row_off_bp = static_cast<uint32_t>(((wp * IB) * 8 + (lane >> 3)) * K);
+
   // K % 128 == 0 here (the dispatcher sends other K to the staged kernel), so every
   // offset is plain arithmetic and only the row range check can zero a chunk
+  auto issue_pair = [&](int s, int st) {
+    const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
+#pragma unroll
+    for (int j = 0; j < IA; ++j)
+      dma16(ra, lds_addr(Abuf[st] + (wp * IA + j) * 1024),
+            row_off_p + static_cast<uint32_t>(j * 8 * K) + k0 + (((wp * IA + j) & 1) ? c_odd : c_even));
+#pragma unroll
+    for (int j = 0; j < IB; ++j)
+      dma16(rb, lds_addr(Bbuf[st] + (wp * IB + j) * 1024),
+            row_off_bp + static_cast<uint32_t>(j * 8 * K) + k0 + (((wp * IB + j) & 1) ? c_odd : c_even));
+    if constexpr (BLOCKWISE) {
+#pragma unroll
+      for (int j = 0; j < IS; ++j)
+        dma4(rsp, lds_addr(Sbuf[st] + wp * WM + j * 64),
+             E8M0 ? static_cast<uint32_t>((j * 64 + lane) * KG4 + (s & ~3))
+                  : static_cast<uint32_t>(((j * 64 + lane) * KG + s) * 4));
+    }
+  };
   auto issue = [&](int s, int st) {
+    if constexpr (PAIR) {
+      if (!lead) return;
+      issue_pair(s, st);
+    }
     const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
     uint8_t* As = Abuf[st];
     uint8_t* Bs = Bbuf[st];
@@ -442,9 +432,12 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     v8i af[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[i] = frag(As, wm * WM + 16 * i + r16);
+    v8i bfb[2];
+    bfb[0] = frag(Bs, wn * WN + r16);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const v8i bf = frag(Bs, wn * WN + 16 * j + r16);
+      if (j + 1 < TN) bfb[(j + 1) & 1] = frag(Bs, wn * WN + 16 * (j + 1) + r16);
+      const v8i bf = bfb[j & 1];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         if constexpr (E8M0) {
@@ -469,7 +462,11 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     if (p < nslabs) issue(p, p);
   for (int s = 0; s < nslabs; ++s) {
     const int ahead = min(NS - 2, nslabs - 1 - s);    // later slabs allowed to stay in flight
-    wait_slabs_ahead<PER_SLAB, NS - 2>(ahead);
+    if constexpr (PAIR) {
+      if (lead) wait_slabs_ahead<2 * PER_SLAB, NS - 2>(ahead);
+    } else {
+      wait_slabs_ahead<PER_SLAB, NS - 2>(ahead);
+    }
     stage_barrier();
     if (s + NS - 1 < nslabs) issue(s + NS - 1, (s + NS - 1) % NS);
     compute(s, s % NS);
@@ -482,7 +479,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WM + 16 * i + r16;
     if (m >= M) continue;
-    uint16_t* crow = c + static_cast<int64_t>(m) * N;
+    uint16_t* crow = c + static_cast<int64_t>(m) * ldc;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int n = wave_n0 + 16 * j + 4 * kq;
@@ -853,7 +850,45 @@ void launch_dma(const uint8_t* qa, const void* sa, const uint8_t* qb, const void
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
   gemm_dma_kernel<BM, BN, WM, WN, SM, OUT, NS><<<tiles_m * tiles_n, (dma_threads<BM, BN, WM, WN>()), 0, s>>>(
-      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m, tiles_n);
+      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m, tiles_n, N);
+}
+
+// The large-tile product: whole rounds of 256x256 tiles (one per CU), and when the tile
+// columns left over make at most half a round, those columns as 256x128 tiles in a second
+// launch, so that the last round is not half empty.  Columns split on whole tiles, so the
+// second launch's weight rows, block scales and C columns are plain offsets.
+constexpr int kCus = 256;
+
+template <int SM>
+const void* scale_cols(const void* sb, int n_off, int K) {
+  if constexpr (SM == SM_BLOCK) return static_cast<const float*>(sb) + static_cast<int64_t>(n_off / kSlab) * (K / kSlab);
+  else if constexpr (SM == SM_E8M0) return static_cast<const uint8_t*>(sb) + static_cast<int64_t>(n_off / kSlab) * e8m0_row_bytes(K / kSlab);
+  else if constexpr (SM == SM_ROW) return static_cast<const float*>(sb) + n_off;
+  else return sb;
+}
+
+template <int SM, int OUT, bool PAIR = false>
+void launch_big(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N, int K,
+                void* c, hipStream_t s) {
+  const int tiles_m = (M + 255) / 256;
+  const int tiles_n = (N + 255) / 256;
+  const int64_t total = static_cast<int64_t>(tiles_m) * tiles_n;
+  int cols_main = tiles_n;
+  if (total % kCus != 0) {
+    const int cand = static_cast<int>((total / kCus) * kCus / tiles_m);   // whole columns in whole rounds
+    if (cand > 0 && static_cast<int64_t>(tiles_m) * (tiles_n - cand) * 2 <= kCus) cols_main = cand;
+  }
+  uint16_t* cc = static_cast<uint16_t*>(c);
+  const int n_main = min(N, cols_main * 256);
+  gemm_dma_kernel<256, 256, 64, 128, SM, OUT, 2, PAIR><<<tiles_m * cols_main, 512, 0, s>>>(
+      qa, sa, qb, sb, M, n_main, K, cc, tiles_m, cols_main, N);
+  if (n_main < N) {
+    const int n_tail = N - n_main;
+    const int tn = (n_tail + 127) / 128;
+    gemm_dma_kernel<256, 128, 64, 64, SM, OUT, 2><<<tiles_m * tn, 512, 0, s>>>(
+        qa, sa, qb + static_cast<int64_t>(n_main) * K, scale_cols<SM>(sb, n_main, K), M, n_tail, K, cc + n_main,
+        tiles_m, tn, N);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int SM, int OUT>
@@ -898,7 +933,9 @@ void launch_gemm_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const v
   }
   const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
   const int64_t tiles = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
-  if (big_tiles >= 256) launch_dma<256, 256, 64, 128, SM, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
+  // paired DMA issue (one wave of each SIMD pair issues the slab's DMA for both) measured
+  // faster where no per-slab FMAs compete with the MFMAs, slower with float32 slab scales
+  if (big_tiles >= 256) launch_big<SM, OUT, SM != SM_BLOCK>(qa, sa, qb, sb, M, N, K, c, s);
   else if (tiles > 256) launch_dma<128, 128, 64, 64, SM, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
   else launch_dma<128, 128, 64, 32, SM, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
 }
