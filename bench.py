@@ -57,6 +57,10 @@ def parse():
     p.add_argument("--scale-fmt", choices=["float32", "ue8m0"], default="float32",
                    help="blockwise workloads: float32 scales (amax/448) or UE8M0 power-of-two "
                         "scale bytes on the scaled MFMA")
+    p.add_argument("--quantize-only", choices=["activations", "weights"], default=None,
+                   help="time only the workload's activation quantize (per token 1x128 groups or per "
+                        "tensor) or its weight quantize (128x128 blocks), next to the byte-mix "
+                        "reference (2 B read, 1 B written per element, no arithmetic) on the same tensors")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the hot path, run a plain device copy of this many MiB "
                         "(the known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -143,6 +147,82 @@ def percentiles(xs):
     a = np.asarray(xs, dtype=np.float64)
     return {"median": round(float(np.median(a)), 6), "p10": round(float(np.percentile(a, 10)), 6),
             "p90": round(float(np.percentile(a, 90)), 6), "n": int(a.size)}
+
+
+def quantize_reference(args):
+    """The quantize pass alone (cold inputs, HIP graphs) and the byte-mix reference on the same
+    tensors; one JSON line with both rates."""
+    import numpy as np
+    import torch
+    import fp8_quantized_gemm_amax_amd as fp8
+    from fp8_quantized_gemm_amax_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    M = args.m if args.m is not None else max(w.m_values)
+    a_bits, b_bits = wl.make_inputs(args.workload, M)
+    weights = args.quantize_only == "weights"
+    bits = b_bits if weights else a_bits
+    R_, C_ = bits.shape
+    gr = 128 if weights else 1
+    blockwise = w.mode == "blockwise" or weights
+    x0 = wl.bits_to_tensor(bits, device=dev)
+    per_set = 3 * R_ * C_
+    R = max(2, min(256, -(-ROTATION_BYTES // per_set)))
+    sets = []
+    for _ in range(R):
+        sx = {"x": x0.clone(), "q": torch.empty((R_, C_), dtype=torch.uint8, device=dev)}
+        sx["s"] = (torch.empty((-(-R_ // gr), -(-C_ // 128)), dtype=torch.float32, device=dev) if blockwise
+                   else torch.empty((1,), dtype=torch.float32, device=dev))
+        sets.append(sx)
+    del x0
+
+    def quant(sx):
+        if blockwise:
+            fp8.fp8_quantize_per_token_group(sx["x"], gr, 128, q=sx["q"], scales=sx["s"])
+        else:
+            fp8.fp8_quantize_per_tensor(sx["x"], q=sx["q"], scale=sx["s"])
+
+    def mix(sx):
+        fp8.fp8_debug_byte_mix(sx["x"], q=sx["q"])
+
+    def timed(fn):
+        for i in range(R):
+            fn(sets[i])
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                fn(sets[i])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, -(-args.steps // R))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) / R for a, b in ev]
+        return sum(per) / len(per), percentiles(per)
+
+    q_ms, q_dist = timed(quant)
+    m_ms, m_dist = timed(mix)
+    nscale = sets[0]["s"].numel()
+    q_bytes = 3 * R_ * C_ + 4 * nscale
+    m_bytes = 3 * R_ * C_
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    m_gbs = m_bytes / (m_ms * 1e-3) / 1e9
+    what = ("weights 128x128 blocks" if weights else
+            "activations 1x128 groups" if blockwise else "activations per tensor")
+    print(json.dumps({
+        "metric": "quantize GB/s (% HBM)", "value": round(q_gbs, 1), "unit": "GB/s",
+        "frac_of_hbm": round(q_gbs / PEAK_HBM_GBS, 4), "ms": round(q_ms, 6), "ms_dist": q_dist,
+        "config": {"workload": args.workload, "tensor": what, "shape": [R_, C_], "rotation_sets": R,
+                   "algorithmic_bytes": q_bytes},
+        "byte_mix_reference": {"GBps": round(m_gbs, 1), "frac_of_hbm": round(m_gbs / PEAK_HBM_GBS, 4),
+                               "ms": round(m_ms, 6), "ms_dist": m_dist, "bytes": m_bytes},
+        "quantize_vs_reference": round(q_gbs / m_gbs, 4),
+        "machine": machine_facts()}), flush=True)
 
 
 def copy_reference(mib, steps):
@@ -305,6 +385,9 @@ def main():
 
     if args.copy_mb:
         copy_reference(args.copy_mb, args.steps)
+        return
+    if args.quantize_only:
+        quantize_reference(args)
         return
 
     import numpy as np

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "fp8_quantize_delayed": ([_P, ctypes.c_int, _I64, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P],
                              ctypes.c_int),
     "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
+    "fp8_debug_byte_mix": ([_P, _P, _I64, _P], ctypes.c_int),
 }
 
 
@@ -466,4 +467,18 @@ def fp8_debug_cast_f32(v, q=None):
         q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
     _check_out(q, v.shape, _CODES, "q", v, (v,))
     _check("fp8_debug_cast_f32", lib().fp8_debug_cast_f32(_ptr(v), _ptr(q), v.numel(), _stream(v)))
+    return q
+
+
+def fp8_debug_byte_mix(x, q=None):
+    """q = the high byte of every 16-bit element of x (measurement reference: a quantizer's
+    byte mix without its arithmetic)."""
+    x = x.contiguous()
+    _need_cuda(x)
+    if x.element_size() != 2:
+        raise TypeError("fp8_debug_byte_mix takes a 16-bit tensor")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check_out(q, x.shape, _U8, "q", x, (x,))
+    _check("fp8_debug_byte_mix", lib().fp8_debug_byte_mix(_ptr(x), _ptr(q), x.numel(), _stream(x)))
     return q

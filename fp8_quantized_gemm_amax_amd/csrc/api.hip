@@ -257,4 +257,15 @@ fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* str
   return finish_launch();
 }
 
+fp8_status_t fp8_debug_byte_mix(const void* x, uint8_t* q, int64_t n, void* stream) {
+  if (n < 0) return FP8_ERR_BAD_SHAPE;
+  if (n > kMaxElems) return FP8_ERR_TOO_LARGE;
+  if (n == 0) return FP8_OK;
+  if (!x || !q) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(q)) return FP8_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  fp8amax::launch_byte_mix(x, n, q, static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
 }  // extern "C"

@@ -403,6 +403,110 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
         static_cast<uint16_t>(f32_to_out_bits<OUT>(mine * (SM == SM_ROW ? row_factor : alpha)));
 }
 
+// One token on the vector ALUs, persistent: a grid that fills the chip; wave gw takes rows
+// gw, gw + waves, ...  The activation row (NCH 1 KB chunks, K <= 1024 NCH) and its scales
+// are loaded into registers once and reused for every row.  The NCH chunk loads of the next
+// row are issued as soon as the current row's chunks have been multiplied, so a whole row
+// stays in flight while the current row's 64 lane partials are reduced and stored.  The
+// arithmetic per chunk is that of gemv_valu_kernel.
+template <int SM, int OUT, int NCH>
+__global__ __launch_bounds__(256) void gemv1_stream_kernel(
+    const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
+    const void* __restrict__ sb_, int N, int K, uint16_t* __restrict__ c, int waves) {
+  constexpr bool BLOCKWISE = slab_scaled(SM);
+  constexpr bool E8M0 = SM == SM_E8M0;
+  const float* __restrict__ sa = static_cast<const float*>(sa_);
+  const float* __restrict__ sb = static_cast<const float*>(sb_);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= N) return;                                        // no barrier in this kernel
+  const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
+  const int SR = E8M0 ? static_cast<int>(e8m0_row_bytes(KG)) : KG * 4;   // bytes per scale row
+
+  // N K < 2^31 (the dispatcher checks), so every offset fits 32 bits
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qb), static_cast<short>(0), N * K, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qa), static_cast<short>(0), K, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t sar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(sa_), static_cast<short>(0), BLOCKWISE ? SR : 0, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(sb_), static_cast<short>(0), BLOCKWISE ? ((N + kSlab - 1) / kSlab) * SR : 0,
+      static_cast<int>(kRsrcWord3));
+
+  v4i av[NCH], wv[NCH];
+  float sav[NCH], sbv[NCH];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int col = ch * 1024 + lane * 16;
+    av[ch] = __builtin_amdgcn_raw_buffer_load_b128(ar, col < K ? static_cast<uint32_t>(col) : kOOB, 0, 0);
+    if constexpr (BLOCKWISE) {
+      const int g = min(col, K - 1) >> 7;
+      sav[ch] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          sar, static_cast<uint32_t>(E8M0 ? (g & ~3) : g * 4), 0, 0));
+    }
+  }
+  auto fetch = [&](int row, int ch) {                         // chunk ch of row (row >= N: zeros)
+    const int col = ch * 1024 + lane * 16;
+    const bool in = (row < N) & (col < K);                    // K % 16 == 0
+    wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? static_cast<uint32_t>(row * K + col) : kOOB, 0, 0);
+    if constexpr (BLOCKWISE) {
+      const int g = min(col, K - 1) >> 7;
+      sbv[ch] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          sbr, in ? static_cast<uint32_t>((row / kSlab) * SR + (E8M0 ? (g & ~3) : g * 4)) : kOOB, 0, 0));
+    }
+  };
+  float alpha = 1.0f;
+  if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
+  const float a_row = SM == SM_ROW ? sa[0] : 1.0f;
+
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) fetch(gw, ch);
+  for (int row = gw; row < N; row += waves) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      float d = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const h2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[ch][q], 1.0f, false);
+        const h2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[ch][q], 1.0f, true);
+        const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[ch][q], 1.0f, false);
+        const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[ch][q], 1.0f, true);
+        d = __builtin_amdgcn_fdot2(w0, a0, d, false);
+        d = __builtin_amdgcn_fdot2(w1, a1, d, false);
+      }
+      if constexpr (E8M0) {
+        const int g = min(ch * 1024 + lane * 16, K - 1) >> 7;
+        const int ea = e8m0_byte(__float_as_uint(sav[ch]), g);
+        const int eb = e8m0_byte(__float_as_uint(sbv[ch]), g);
+        acc += (ea == 0xff || eb == 0xff) ? __uint_as_float(kCanonicalNaN) : __builtin_amdgcn_ldexpf(d, ea + eb - 254);
+      } else if constexpr (BLOCKWISE) {
+        acc = __builtin_fmaf(d, sav[ch] * sbv[ch], acc);
+      } else {
+        acc += d;
+      }
+      fetch(row + waves, ch);                                  // the same chunk of the next row
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    const float f = SM == SM_ROW ? a_row * sb[row] : alpha;
+    if (lane == 0) c[row] = static_cast<uint16_t>(f32_to_out_bits<OUT>(acc * f));
+  }
+}
+
+constexpr int kStreamPerCu = 24;             // waves per CU of the persistent one-token kernel
+
+template <int BW, int OUT, int NCH>
+void launch_stream1_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int N, int K,
+                      void* c, hipStream_t s, int per_cu) {
+  const int waves = min(N, 256 * per_cu);
+  gemv1_stream_kernel<BW, OUT, NCH><<<(waves + 3) / 4, 256, 0, s>>>(qa, sa, qb, sb, N, K,
+                                                                    static_cast<uint16_t*>(c), waves);
+}
+
 template <int BW, int OUT, int MT, int RPW, int UNROLL>
 void launch_valu_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
                    int K, void* c, hipStream_t s) {
@@ -418,14 +522,34 @@ void launch_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* 
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
 }
 
-// Measured on MI355X with cold weights: one token runs best on the vector-ALU kernel
+// Measured on MI355X with cold weights: one token runs best on the vector-ALU kernels
 // (1 KB row streams; one row per wave with four 1 KB loads in flight beat two or more rows
-// per wave by 5% at W[11008, 4096] and tied at W[18432, 7168]); from two tokens on the MFMA
-// kernel, with two row blocks per wave once the activation fragment is worth sharing (M > 4).
+// per wave by 5% at W[11008, 4096] and tied at W[18432, 7168]).  With float32 block scales
+// the persistent kernel with the activation row held in registers is 10-12% faster on both
+// shapes (24 waves per CU led 16 and 32); per tensor and with UE8M0 scales the one-wave-per-
+// row kernel stays ahead.  From two tokens on the MFMA kernel, with two row blocks per wave
+// once the activation fragment is worth sharing (M > 4).
 template <int BW, int OUT>
 void launch_m(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
               int K, void* c, hipStream_t s) {
-  if (M == 1) launch_valu_t<BW, OUT, 1, 1, 4>(qa, sa, qb, sb, M, N, K, c, s);
+  if constexpr (BW == SM_BLOCK) {
+    if (M == 1 && K <= 8192 && static_cast<int64_t>(N) * K < (int64_t{1} << 31)) {
+      switch ((K + 1023) / 1024) {
+        case 1: launch_stream1_t<BW, OUT, 1>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        case 2: launch_stream1_t<BW, OUT, 2>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        case 3: launch_stream1_t<BW, OUT, 3>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        case 4: launch_stream1_t<BW, OUT, 4>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        case 5: launch_stream1_t<BW, OUT, 5>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        case 6: launch_stream1_t<BW, OUT, 6>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        case 7: launch_stream1_t<BW, OUT, 7>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+        default: launch_stream1_t<BW, OUT, 8>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+      }
+      return;
+    }
+  }
+  if (M == 1) {
+    launch_valu_t<BW, OUT, 1, 1, 4>(qa, sa, qb, sb, M, N, K, c, s);
+  }
   else if (M <= 4) launch_t<BW, OUT, 2, 4, 1>(qa, sa, qb, sb, M, N, K, c, s);
   else launch_t<BW, OUT, 4, 2, 2>(qa, sa, qb, sb, M, N, K, c, s);
 }

@@ -58,6 +58,9 @@ void launch_delayed_quantize(int dt, const void* x, int64_t n, float* history, i
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 
+// Measurement reference: q[i] = high byte of the 16-bit x[i] (the quantizers' byte mix).
+void launch_byte_mix(const void* x, int64_t n, uint8_t* q, hipStream_t s);
+
 // Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its
 // launcher.  sa and sb point at float32 scales, or at e8m0fnu bytes for SM_E8M0.
 // Grouped (mixture-of-experts) blockwise product, SM_BLOCK or SM_E8M0: expert e's rows

@@ -784,6 +784,36 @@ __global__ __launch_bounds__(kThreads) void debug_cast_kernel(const float* __res
   for (int64_t i = tid; i < n; i += stride) q[i] = static_cast<uint8_t>(e4m3_encode(v[i]));
 }
 
+// Measurement reference with the quantizers' byte mix: q[i] = the high byte of the 16-bit
+// element x[i] (2 bytes read, 1 written per element, no arithmetic).  Each lane moves 8
+// elements per step (one 16-byte load, one 8-byte store), two steps in flight per wave,
+// like the 1x128 group kernel; a scalar loop takes the last n % 512 elements.
+__global__ __launch_bounds__(kThreads) void byte_mix_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                            uint8_t* __restrict__ q) {
+  constexpr int kPer = 64 * 8;                               // elements per wave step
+  const int64_t steps = n / kPer;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  const int64_t waves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  const int lane = threadIdx.x & 63;
+  auto high = [](uint32_t a, uint32_t b) {
+    return (a >> 8 & 0xffu) | (a >> 16 & 0xff00u) | (b >> 8 & 0xffu) << 16 | (b >> 24) << 24;
+  };
+  for (int64_t i0 = wave; i0 < steps; i0 += 2 * waves) {
+    U4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (i0 + u * waves < steps) v[u] = load16(x + (i0 + u * waves) * kPer + lane * 8);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (i0 + u * waves < steps)
+        *reinterpret_cast<uint2*>(q + (i0 + u * waves) * kPer + lane * 8) =
+            make_uint2(high(v[u].x, v[u].y), high(v[u].z, v[u].w));
+  }
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  for (int64_t i = steps * kPer + tid; i < n; i += static_cast<int64_t>(gridDim.x) * kThreads)
+    q[i] = static_cast<uint8_t>(x[i] >> 8);
+}
+
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -796,9 +826,11 @@ constexpr int64_t kReduceCap = 256 * 4;      // whole-tensor reduction workgroup
 constexpr int64_t kGroupCap = 256 * 256;     // group/block kernels loop beyond this grid
 
 // 1x128 vector path: about sets_per_cu 16-lane sets per CU, each taking cg consecutive
-// groups of one row.
+// groups of one row.  Measured with cold inputs on A[4096, 7168] and A[4096, 4096]: 128
+// sets per CU with two groups in flight per set led 64, 256 and 512 sets and 4 or 8 groups
+// in flight, at 86-90% of a copy with the same byte mix and no arithmetic.
 constexpr int kGroupUnroll = 2;
-constexpr int64_t kGroupSetsPerCu = 64;
+constexpr int64_t kGroupSetsPerCu = 128;
 
 template <int DT, bool WRITE_Q, int UNROLL, bool E8M0 = false>
 void launch_group_vec(const uint16_t* xp, int64_t rows, int64_t cols, int64_t sets_per_cu, uint8_t* q,
@@ -965,6 +997,11 @@ void launch_delayed_quantize(int dt, const void* x, int64_t n, float* history, i
   }
   launch_tensor_static(dt, x, n, scale, q, amax_acc, s);
   delayed_update_kernel<<<1, 64, 0, s>>>(history, len, amax_acc, step, interval, margin, scale, scale_used);
+}
+
+void launch_byte_mix(const void* x, int64_t n, uint8_t* q, hipStream_t s) {
+  const unsigned grid = grid_for(n, kThreads * 8, 256 * 32);      // up to 32 workgroups per CU
+  byte_mix_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(x), n, q);
 }
 
 void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s) {

@@ -301,6 +301,17 @@ fp8_status_t fp8_quantize_delayed(const void* x, fp8_dtype_t dt, int64_t rows, i
  */
 fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* stream);
 
+/*
+ * fp8_debug_byte_mix - measurement reference, no part of the method: q[i] = the high byte
+ * of the 16-bit element x[i], for n elements.  It moves the same bytes as a quantizer
+ * (2 read, 1 written per element) with the same access pattern and no arithmetic, so its
+ * rate is the ceiling a quantize pass can approach on the device.  x is [n] 16-bit, q is
+ * uint8 [n], both 16-byte aligned, device memory owned by the caller; asynchronous on
+ * `stream`.  Errors: FP8_ERR_BAD_SHAPE for n < 0, FP8_ERR_TOO_LARGE, FP8_ERR_NULL_POINTER,
+ * FP8_ERR_MISALIGNED, all before any HIP call; n == 0 returns FP8_OK.
+ */
+fp8_status_t fp8_debug_byte_mix(const void* x, uint8_t* q, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

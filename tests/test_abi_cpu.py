@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(L):
                           "fp8_quantize_per_token_group_ue8m0", "fp8_gemm_scaled_blockwise_ue8m0",
                           "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
                           "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise",
-                          "fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0"}
+                          "fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0",
+                          "fp8_debug_byte_mix"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -106,6 +107,12 @@ def test_quantize_validation(L):
     assert d(A16, A16, -1, None) == SHAPE
     assert d(A16, A16, 0, None) == OK
     assert d(None, A16, 8, None) == NULLP
+    bm = L.fp8_debug_byte_mix
+    assert bm(A16, A16, -1, None) == SHAPE
+    assert bm(A16, A16, 0, None) == OK
+    assert bm(None, A16, 8, None) == NULLP
+    assert bm(A16, A16 + 8, 8, None) == ALIGN
+    assert bm(A16, A16, 2 ** 62, None) == LARGE
 
 
 def test_static_and_delayed_validation(L):
