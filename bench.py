@@ -68,7 +68,8 @@ def parse():
 
 
 KERNEL_SOURCES = ["fp8_quantized_gemm_amax_amd/csrc/gemm.hip", "fp8_quantized_gemm_amax_amd/csrc/gemv.hip",
-                  "fp8_quantized_gemm_amax_amd/csrc/dma.hpp", "fp8_quantized_gemm_amax_amd/csrc/fp8_device.hpp"]
+                  "fp8_quantized_gemm_amax_amd/csrc/gemm_common.hpp", "fp8_quantized_gemm_amax_amd/csrc/dma.hpp",
+                  "fp8_quantized_gemm_amax_amd/csrc/fp8_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -114,9 +115,24 @@ def measured_traffic(workload, M, scheme="tensorwise"):
     return e.get("traffic_bytes_per_launch")
 
 
+def shader_clock():
+    """The current shader clock level of the first GPU that lists one in sysfs (MHz), or None.
+    Read from a file: no child process is started (a process that has initialised the GPU
+    must not exec another program on the box)."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for ln in f:
+                    if ln.rstrip().endswith("*"):
+                        return ln.split(":", 1)[1].strip().rstrip("*").strip()
+        except OSError:
+            continue
+    return None
+
+
 def machine_facts():
     """Compute units and clocks of GPU 0, the ROCm and HIP versions, the host CPU model."""
-    import subprocess
     import torch
     props = torch.cuda.get_device_properties(0)
     facts = {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
@@ -132,13 +148,7 @@ def machine_facts():
     except OSError:
         facts["host_cpu"] = None
     facts["host_threads"] = len(os.sched_getaffinity(0))
-    try:                         # current and highest shader clock levels (MHz)
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                             timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        facts["sclk"] = card.get("sclk clock speed:") or card.get("sclk clock level:")
-    except Exception:            # tool missing or output changed: leave the clock unrecorded
-        facts["sclk"] = None
+    facts["sclk"] = shader_clock()
     return facts
 
 
