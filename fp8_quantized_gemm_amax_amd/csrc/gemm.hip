@@ -10,18 +10,21 @@
 //   rowwise: scale = sa[m] * sb[n], one scale per token and per output channel (the
 //     Transformer Engine page §5, per-channel scaling), applied once like tensorwise.
 //
-// Design (CDNA4): a workgroup of 4 waves computes a BM x BN tile.  Each K step is one
-// 128-byte slab: the A and B slabs are staged global -> VGPR -> LDS with a double buffer
-// (the next slab's global loads are in flight while the current slab is multiplied), and
-// each wave runs v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales, i.e. a plain FP8
-// product) on 16x16 output sub-tiles.  One 16x16x128 MFMA covers exactly one slab, so the
+// Kernels (CDNA4).  Every kernel walks K in 128-byte slabs and multiplies with
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales, i.e. a plain FP8 product, or the
+// UE8M0 block scales themselves); one instruction covers exactly one slab, so the float32
 // blockwise epilogue is one FMA per accumulator per slab.
-//
-// LDS layout: a slab tile is [rows][128 B]; the 16-byte chunk c of row r is stored at
-// chunk position c ^ ((r >> 1) & 7).  A row is half of the 64 banks, so rows r and r + 1
-// start on opposite halves and the swizzle spreads each pair over the eight 16-byte bank
-// groups: the 16 lanes reading one chunk column of 16 consecutive rows hit 16 distinct
-// bank groups (a swizzle on r & 7 alone maps rows r and r + 8 to the same banks).
+//   gemm_dma_kernel: the tiled product for 129+ tokens.  A and B slabs move global -> LDS
+//     by LDS DMA into an NS-stage ring, eight (or four) waves multiply fragments read from
+//     LDS.  256x256 tiles when there is at least one per CU, launched as whole rounds plus
+//     a second launch of 256x128 tiles for a leftover half round (launch_big); 128x128
+//     tiles otherwise.
+//   gemm_skinny_kernel / gemm_grouped_kernel: 17-128 tokens (and the mixture-of-experts
+//     chunks), weight rows streamed into registers, the tokens staged in LDS by one wave.
+//   gemm_fp8_kernel: K not a multiple of 128 (or too large for 32-bit buffer offsets),
+//     slabs staged global -> VGPR -> LDS with a zero-filled K tail.
+// 1-16 tokens go to the decode kernels of gemv.hip.  The LDS slab layout and the tile order
+// are in gemm_common.hpp.
 //
 // MFMA operand roles: the first operand is the B (weight) sub-tile, the second the A
 // sub-tile, so lane l holds C[m = l % 16][n = 4 * (l / 16) + r] for r = 0..3: four

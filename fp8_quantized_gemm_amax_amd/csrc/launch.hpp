@@ -61,14 +61,14 @@ void launch_debug_cast(const float* v, int64_t n, uint8_t* q, hipStream_t s);
 // Measurement reference: q[i] = high byte of the 16-bit x[i] (the quantizers' byte mix).
 void launch_byte_mix(const void* x, int64_t n, uint8_t* q, hipStream_t s);
 
-// Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its
-// launcher.  sa and sb point at float32 scales, or at e8m0fnu bytes for SM_E8M0.
 // Grouped (mixture-of-experts) blockwise product, SM_BLOCK or SM_E8M0: expert e's rows
 // [offsets[e], offsets[e + 1]) of A and C times qb[e] ([E][N][K]); offsets [E + 1] int32 on
 // the device.  Returns false when the launch grid would be too large.
 bool launch_grouped(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb,
                     const int* offsets, int E, int T, int N, int K, void* c, hipStream_t s);
 
+// Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its
+// launcher.  sa and sb point at float32 scales, or at e8m0fnu bytes for SM_E8M0.
 bool gemv_fits(int M, int K);
 void launch_gemv(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
                  const void* sb, int M, int N, int K, void* c, hipStream_t s);
