@@ -73,12 +73,41 @@ KERNEL_SOURCES = ["fp8_quantized_gemm_amax_amd/csrc/gemm.hip", "fp8_quantized_ge
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
+def strip_comments(src):
+    """C/C++ source without its comments and with runs of white space folded to one blank, so
+    that an edit of a comment leaves the hash of the code unchanged.  String and character
+    literals are kept as written."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """Hash of the GEMM kernels' code (comments and layout excluded): the counter table's
+    entries hold only while it is unchanged."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

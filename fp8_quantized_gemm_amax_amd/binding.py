@@ -44,6 +44,7 @@ _SIGNATURES = {
                              ctypes.c_int),
     "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
     "fp8_debug_byte_mix": ([_P, _P, _I64, _P], ctypes.c_int),
+    "fp8_debug_gemm_plan": ([_I32, _I64, _I64, _I64, _P], ctypes.c_int),
 }
 
 
@@ -482,3 +483,31 @@ def fp8_debug_byte_mix(x, q=None):
     _check_out(q, x.shape, _U8, "q", x, (x,))
     _check("fp8_debug_byte_mix", lib().fp8_debug_byte_mix(_ptr(x), _ptr(q), x.numel(), _stream(x)))
     return q
+
+
+class _GemmLaunch(ctypes.Structure):
+    _fields_ = [("kernel", _I32), ("tile_m", _I32), ("tile_n", _I32), ("variant", _I32), ("waves", _I32),
+                ("paired", _I32), ("grid", _I64), ("threads", _I64), ("n_begin", _I64), ("n_end", _I64),
+                ("max_range", _I64), ("max_offset", _I64)]
+
+
+class _GemmPlan(ctypes.Structure):
+    _fields_ = [("launches", _I32), ("reserved", _I32), ("launch", _GemmLaunch * 2)]
+
+
+GEMM_MODES = {"tensorwise": 0, "blockwise": 1, "blockwise_ue8m0": 2, "rowwise": 3}
+GEMM_KERNELS = {1: "gemv_stream", 2: "gemv_valu", 3: "gemv_mfma", 4: "skinny", 5: "tile", 6: "staged"}
+
+
+def fp8_debug_gemm_plan(mode, M, N, K):
+    """The launches a scaled GEMM of this shape makes (host arithmetic only, no GPU): a list
+    of dicts with the kernel's name and the fields of fp8_gemm_launch_t."""
+    plan = _GemmPlan()
+    _check("fp8_debug_gemm_plan", lib().fp8_debug_gemm_plan(GEMM_MODES[mode], M, N, K, ctypes.byref(plan)))
+    out = []
+    for i in range(plan.launches):
+        l = plan.launch[i]
+        d = {name: getattr(l, name) for name, _ in _GemmLaunch._fields_}
+        d["kernel"] = GEMM_KERNELS[l.kernel]
+        out.append(d)
+    return out

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gemm_plan.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -30,22 +31,33 @@ fp8_status_t finish_launch() {
   return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH;
 }
 
-fp8_status_t gemm_common(int mode, const uint8_t* qa, const void* sa, const uint8_t* qb,
-                         const void* sb, int64_t M, int64_t N, int64_t K, void* c,
-                         fp8_dtype_t out_dt, void* stream) {
+// Shape rules of the scaled GEMMs, and the plan of their launches (FP8_OK only).
+fp8_status_t gemm_shape(int mode, int64_t M, int64_t N, int64_t K, fp8_gemm_plan_t* plan) {
   const bool blockwise = fp8amax::slab_scaled(mode);
   if (M < 0 || N < 0 || K <= 0) return FP8_ERR_BAD_SHAPE;
   if (blockwise ? (K % 128 != 0) : (K % 16 != 0)) return FP8_ERR_BAD_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8_ERR_TOO_LARGE;
+  if (M > kMaxElems / K || N > kMaxElems / K || (N > 0 && M > kMaxElems / N)) return FP8_ERR_TOO_LARGE;
+  *plan = fp8amax::plan::plan_gemm(mode, M, N, K);
+  if (!fp8amax::plan::plan_fits(*plan)) return FP8_ERR_TOO_LARGE;
+  return FP8_OK;
+}
+
+fp8_status_t gemm_common(int mode, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                         const void* sb, int64_t M, int64_t N, int64_t K, void* c,
+                         fp8_dtype_t out_dt, void* stream) {
+  fp8_gemm_plan_t plan;
+  const fp8_status_t st = gemm_shape(mode, M, N, K, &plan);
+  if (st != FP8_OK) return st;
   if (!valid_dt(out_dt)) return FP8_ERR_BAD_DTYPE;
   if (M == 0 || N == 0) return FP8_OK;
   if (!qa || !sa || !qb || !sb || !c) return FP8_ERR_NULL_POINTER;
   if (!aligned16(qa) || !aligned16(qb) || !aligned16(c) || !aligned4(sa) || !aligned4(sb))
     return FP8_ERR_MISALIGNED;
   (void)hipGetLastError();   // clear a stale error so FP8_ERR_LAUNCH reports this call only
-  fp8amax::launch_gemm(mode, static_cast<int>(out_dt), qa, sa, qb, sb, static_cast<int>(M),
-                       static_cast<int>(N), static_cast<int>(K), c,
-                       static_cast<hipStream_t>(stream));
+  if (!fp8amax::launch_gemm(mode, static_cast<int>(out_dt), plan, qa, sa, qb, sb, static_cast<int>(M),
+                            static_cast<int>(N), static_cast<int>(K), c, static_cast<hipStream_t>(stream)))
+    return FP8_ERR_LAUNCH;
   return finish_launch();
 }
 
@@ -255,6 +267,12 @@ fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* str
   (void)hipGetLastError();
   fp8amax::launch_debug_cast(v, n, q, static_cast<hipStream_t>(stream));
   return finish_launch();
+}
+
+fp8_status_t fp8_debug_gemm_plan(int32_t mode, int64_t M, int64_t N, int64_t K, fp8_gemm_plan_t* plan) {
+  if (mode < FP8_SCALE_TENSOR || mode > FP8_SCALE_ROW) return FP8_ERR_BAD_SHAPE;
+  if (!plan) return FP8_ERR_NULL_POINTER;
+  return gemm_shape(mode, M, N, K, plan);
 }
 
 fp8_status_t fp8_debug_byte_mix(const void* x, uint8_t* q, int64_t n, void* stream) {

@@ -17,14 +17,15 @@
 //   gemm_dma_kernel: the tiled product for 129+ tokens.  A and B slabs move global -> LDS
 //     by LDS DMA into an NS-stage ring, eight (or four) waves multiply fragments read from
 //     LDS.  256x256 tiles when there is at least one per CU, launched as whole rounds plus
-//     a second launch of 256x128 tiles for a leftover half round (launch_big); 128x128
+//     a second launch of 256x128 tiles for a leftover half round; 128x128
 //     tiles otherwise.
 //   gemm_skinny_kernel / gemm_grouped_kernel: 17-128 tokens (and the mixture-of-experts
 //     chunks), weight rows streamed into registers, the tokens staged in LDS by one wave.
 //   gemm_fp8_kernel: K not a multiple of 128 (or too large for 32-bit buffer offsets),
 //     slabs staged global -> VGPR -> LDS with a zero-filled K tail.
 // 1-16 tokens go to the decode kernels of gemv.hip.  The LDS slab layout and the tile order
-// are in gemm_common.hpp.
+// are in gemm_common.hpp; which kernel, tile and grid a shape gets is plan_gemm in
+// gemm_plan.hpp, whose 32-bit range and offset figures bound the buffer arithmetic here.
 //
 // MFMA operand roles: the first operand is the B (weight) sub-tile, the second the A
 // sub-tile, so lane l holds C[m = l % 16][n = 4 * (l / 16) + r] for r = 0..3: four
@@ -36,6 +37,7 @@
 #include "dma.hpp"
 #include "fp8_device.hpp"
 #include "gemm_common.hpp"
+#include "gemm_plan.hpp"
 #include "launch.hpp"
 
 namespace fp8amax {
@@ -347,7 +349,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   const uint32_t row_off_p = static_cast<uint32_t>(((wp * IA) * 8 + (lane >> 3)) * K);
   const uint32_t row_off_bp = static_cast<uint32_t>(((wp * IB) * 8 + (lane >> 3)) * K);
 
-  // K % 128 == 0 here (the dispatcher sends other K to the staged kernel), so every
+  // K % 128 == 0 here (plan_gemm sends other K to the staged kernel), so every
   // offset is plain arithmetic and only the row range check can zero a chunk
   auto issue_pair = [&](int s, int st) {
     const uint32_t k0 = static_cast<uint32_t>(s * kSlab);
@@ -516,7 +518,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
 // compute waves have finished with slab s - 1, whose stage the loader refills next.
 // The launch has cw + 1 waves (cw <= kSkinnyMaxCw): the number of compute waves sets how
 // many weight rows a workgroup covers, and is chosen so one round of workgroups spans N.
-constexpr int kSkinnyMaxCw = 7;
+constexpr int kSkinnyMaxCw = plan::kSkinnyMaxCw;
 
 template <int SM, int MB>
 struct SkinnyShape {
@@ -840,107 +842,85 @@ __global__ __launch_bounds__((kSkinnyMaxCw + 1) * 64) void gemm_grouped_kernel(
 }
 
 template <int SM, int OUT, int NB, int MB, int NS, int UNROLL>
-void launch_skinny(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-                   int K, int cw, void* c, hipStream_t s) {
-  const int rows = 16 * cw * NB;
-  gemm_skinny_kernel<SM, OUT, NB, MB, NS, UNROLL><<<(N + rows - 1) / rows, (cw + 1) * 64, 0, s>>>(
-      qa, sa, qb, sb, M, N, K, cw, static_cast<uint16_t*>(c));
+void launch_skinny(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                   const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  gemm_skinny_kernel<SM, OUT, NB, MB, NS, UNROLL><<<static_cast<unsigned>(L.grid), static_cast<unsigned>(L.threads), 0, s>>>(
+      qa, sa, qb, sb, M, N, K, L.waves, static_cast<uint16_t*>(c));
 }
 
-template <int BM, int BN, int WM, int WN, int SM, int OUT, int NS = 2>
-void launch_dma(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-                int K, void* c, hipStream_t s) {
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  gemm_dma_kernel<BM, BN, WM, WN, SM, OUT, NS><<<tiles_m * tiles_n, (dma_threads<BM, BN, WM, WN>()), 0, s>>>(
-      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m, tiles_n, N);
-}
-
-// The large-tile product: whole rounds of 256x256 tiles (one per CU), and when the tile
-// columns left over make at most half a round, those columns as 256x128 tiles in a second
-// launch, so that the last round is not half empty.  Columns split on whole tiles, so the
-// second launch's weight rows, block scales and C columns are plain offsets.
-constexpr int kCus = 256;
-
+// Weight-block scales of the columns from n_off on (n_off a multiple of 128).
 template <int SM>
-const void* scale_cols(const void* sb, int n_off, int K) {
-  if constexpr (SM == SM_BLOCK) return static_cast<const float*>(sb) + static_cast<int64_t>(n_off / kSlab) * (K / kSlab);
-  else if constexpr (SM == SM_E8M0) return static_cast<const uint8_t*>(sb) + static_cast<int64_t>(n_off / kSlab) * e8m0_row_bytes(K / kSlab);
+const void* scale_cols(const void* sb, int64_t n_off, int K) {
+  if constexpr (SM == SM_BLOCK) return static_cast<const float*>(sb) + (n_off / kSlab) * (K / kSlab);
+  else if constexpr (SM == SM_E8M0) return static_cast<const uint8_t*>(sb) + (n_off / kSlab) * e8m0_row_bytes(K / kSlab);
   else if constexpr (SM == SM_ROW) return static_cast<const float*>(sb) + n_off;
   else return sb;
 }
 
-template <int SM, int OUT, bool PAIR = false>
-void launch_big(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N, int K,
-                void* c, hipStream_t s) {
-  const int tiles_m = (M + 255) / 256;
-  const int tiles_n = (N + 255) / 256;
-  const int64_t total = static_cast<int64_t>(tiles_m) * tiles_n;
-  int cols_main = tiles_n;
-  if (total % kCus != 0) {
-    const int cand = static_cast<int>((total / kCus) * kCus / tiles_m);   // whole columns in whole rounds
-    if (cand > 0 && static_cast<int64_t>(tiles_m) * (tiles_n - cand) * 2 <= kCus) cols_main = cand;
-  }
-  uint16_t* cc = static_cast<uint16_t*>(c);
-  const int n_main = min(N, cols_main * 256);
-  gemm_dma_kernel<256, 256, 64, 128, SM, OUT, 2, PAIR><<<tiles_m * cols_main, 512, 0, s>>>(
-      qa, sa, qb, sb, M, n_main, K, cc, tiles_m, cols_main, N);
-  if (n_main < N) {
-    const int n_tail = N - n_main;
-    const int tn = (n_tail + 127) / 128;
-    gemm_dma_kernel<256, 128, 64, 64, SM, OUT, 2><<<tiles_m * tn, 512, 0, s>>>(
-        qa, sa, qb + static_cast<int64_t>(n_main) * K, scale_cols<SM>(sb, n_main, K), M, n_tail, K, cc + n_main,
-        tiles_m, tn, N);
-  }
+// One launch of the tiled DMA kernel over the plan's columns [n_begin, n_end): the weight
+// rows, block scales and C columns of that range are plain offsets (it starts on a whole
+// weight block), and C keeps its full row pitch N.
+template <int BM, int BN, int WM, int WN, int SM, int OUT, int NS, bool PAIR>
+void launch_tile(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                 const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  const int n = static_cast<int>(L.n_end - L.n_begin);
+  gemm_dma_kernel<BM, BN, WM, WN, SM, OUT, NS, PAIR><<<static_cast<unsigned>(L.grid), (dma_threads<BM, BN, WM, WN>()), 0, s>>>(
+      qa, sa, qb + L.n_begin * K, scale_cols<SM>(sb, L.n_begin, K), M, n, K,
+      static_cast<uint16_t*>(c) + L.n_begin, (M + BM - 1) / BM, (n + BN - 1) / BN, N);
 }
 
 template <int BM, int BN, int WM, int WN, int SM, int OUT>
-void launch_cfg(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-                int K, void* c, hipStream_t s) {
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  gemm_fp8_kernel<BM, BN, WM, WN, SM, OUT><<<tiles_m * tiles_n, kThreads, 0, s>>>(
-      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), tiles_m);
+void launch_cfg(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  gemm_fp8_kernel<BM, BN, WM, WN, SM, OUT><<<static_cast<unsigned>(L.grid), kThreads, 0, s>>>(
+      qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c), (M + BM - 1) / BM);
+}
+
+// Carries out one launch of a plan (plan_gemm in gemm_plan.hpp chooses the kernel, tile,
+// grid and columns, and measures why).  Returns false for a launch no kernel here matches.
+template <int SM, int OUT>
+bool run_launch(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  constexpr bool BW = slab_scaled(SM);
+  constexpr bool PAIR = SM != SM_BLOCK;            // the 256x256 kernel's DMA issue, per mode
+  switch (L.kernel) {
+    case FP8_KERNEL_GEMV_STREAM:
+    case FP8_KERNEL_GEMV_VALU:
+    case FP8_KERNEL_GEMV_MFMA:
+      return launch_gemv(SM, OUT, L, qa, sa, qb, sb, M, N, K, c, s);
+    case FP8_KERNEL_STAGED:
+      if (L.tile_m == 16) launch_cfg<16, 256, 16, 64, SM, OUT>(L, qa, sa, qb, sb, M, N, K, c, s);
+      else launch_cfg<128, 128, 64, 64, SM, OUT>(L, qa, sa, qb, sb, M, N, K, c, s);
+      return true;
+    case FP8_KERNEL_SKINNY:
+      if (L.variant == 2) launch_skinny<SM, OUT, 1, 2, 4, 4>(L, qa, sa, qb, sb, M, N, K, c, s);
+      else if (L.variant == 4) launch_skinny<SM, OUT, 1, 4, 4, 4>(L, qa, sa, qb, sb, M, N, K, c, s);
+      else if constexpr (BW) launch_skinny<SM, OUT, 1, 8, 5, 2>(L, qa, sa, qb, sb, M, N, K, c, s);
+      else launch_skinny<SM, OUT, 1, 8, 5, 4>(L, qa, sa, qb, sb, M, N, K, c, s);
+      return true;
+    case FP8_KERNEL_TILE:
+      if (L.tile_m == 256 && L.tile_n == 256) {
+        if (L.paired != (PAIR ? 1 : 0)) return false;
+        launch_tile<256, 256, 64, 128, SM, OUT, 2, PAIR>(L, qa, sa, qb, sb, M, N, K, c, s);
+      } else if (L.tile_m == 256) {
+        launch_tile<256, 128, 64, 64, SM, OUT, 2, false>(L, qa, sa, qb, sb, M, N, K, c, s);
+      } else if (L.waves == 4) {
+        launch_tile<128, 128, 64, 64, SM, OUT, 2, false>(L, qa, sa, qb, sb, M, N, K, c, s);
+      } else {
+        launch_tile<128, 128, 64, 32, SM, OUT, 3, false>(L, qa, sa, qb, sb, M, N, K, c, s);
+      }
+      return true;
+    default:
+      return false;
+  }
 }
 
 template <int SM, int OUT>
-void launch_gemm_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-                   int K, void* c, hipStream_t s) {
-  constexpr bool BW = slab_scaled(SM);
-  if (gemv_fits(M, K)) {
-    launch_gemv(SM, OUT, qa, sa, qb, sb, M, N, K, c, s);
-    return;
-  }
-  // K tail: the register-staged kernel zero-fills it.  It also takes K so large that 256
-  // rows of K bytes overflow the 32-bit buffer offsets of the DMA kernel.
-  if (K % kSlab != 0 || static_cast<int64_t>(K) * 256 >= (int64_t{1} << 31)) {
-    if (M <= 16) launch_cfg<16, 256, 16, 64, SM, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-    else launch_cfg<128, 128, 64, 64, SM, OUT>(qa, sa, qb, sb, M, N, K, c, s);
-    return;
-  }
-  // Tile choice, measured on MI355X with cold operands:
-  //  - up to 128 rows (weights streamed once): the few-token kernel, with as few compute
-  //    waves (16 weight rows each) as keep the workgroups within one round on 256 CUs,
-  //    since every workgroup also reads all of A;
-  //  - at least one 256x256 tile per CU: 256x256, eight waves of 64x128, two stages;
-  //  - more than one 128x128 tile per CU: 128x128 tiles of four 64x64 waves with two
-  //    stages, so that two workgroups share a CU;
-  //  - otherwise (one partial round) 128x128 tiles of eight 64x32 waves, three stages.
-  if (M <= 128) {
-    const int cw = min(kSkinnyMaxCw, max(2, (N + 16 * 256 - 1) / (16 * 256)));
-    if (M <= 32) launch_skinny<SM, OUT, 1, 2, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    else if (M <= 64) launch_skinny<SM, OUT, 1, 4, 4, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    else if constexpr (BW) launch_skinny<SM, OUT, 1, 8, 5, 2>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    else launch_skinny<SM, OUT, 1, 8, 5, 4>(qa, sa, qb, sb, M, N, K, cw, c, s);
-    return;
-  }
-  const int64_t big_tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t tiles = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
-  // paired DMA issue (one wave of each SIMD pair issues the slab's DMA for both) measured
-  // faster where no per-slab FMAs compete with the MFMAs, slower with float32 slab scales
-  if (big_tiles >= 256) launch_big<SM, OUT, SM != SM_BLOCK>(qa, sa, qb, sb, M, N, K, c, s);
-  else if (tiles > 256) launch_dma<128, 128, 64, 64, SM, OUT, 2>(qa, sa, qb, sb, M, N, K, c, s);
-  else launch_dma<128, 128, 64, 32, SM, OUT, 3>(qa, sa, qb, sb, M, N, K, c, s);
+bool launch_gemm_t(const fp8_gemm_plan_t& p, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                   const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  for (int i = 0; i < p.launches; ++i)
+    if (!run_launch<SM, OUT>(p.launch[i], qa, sa, qb, sb, M, N, K, c, s)) return false;
+  return true;
 }
 
 // Grouped launch: 16 MB tokens per chunk, cw compute waves of NB weight-row blocks each.
@@ -969,10 +949,10 @@ bool launch_grouped_m(const uint8_t* qa, const void* sa, const uint8_t* qb, cons
 }
 
 template <int SM>
-void launch_gemm_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M,
-                   int N, int K, void* c, hipStream_t s) {
-  if (out_dt == DT_BF16) launch_gemm_t<SM, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-  else launch_gemm_t<SM, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
+bool launch_gemm_m(const fp8_gemm_plan_t& p, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                   const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (out_dt == DT_BF16) return launch_gemm_t<SM, DT_BF16>(p, qa, sa, qb, sb, M, N, K, c, s);
+  return launch_gemm_t<SM, DT_F16>(p, qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
@@ -986,12 +966,12 @@ bool launch_grouped(int mode, int out_dt, const uint8_t* qa, const void* sa, con
                            : launch_grouped_m<SM_BLOCK, DT_F16>(qa, sa, qb, sb, offsets, E, T, N, K, c, s);
 }
 
-void launch_gemm(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
-                 const void* sb, int M, int N, int K, void* c, hipStream_t s) {
-  if (mode == SM_ROW) launch_gemm_m<SM_ROW>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
-  else if (mode == SM_E8M0) launch_gemm_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
-  else if (mode == SM_BLOCK) launch_gemm_m<SM_BLOCK>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
-  else launch_gemm_m<SM_TENSOR>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+bool launch_gemm(int mode, int out_dt, const fp8_gemm_plan_t& p, const uint8_t* qa, const void* sa,
+                 const uint8_t* qb, const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (mode == SM_ROW) return launch_gemm_m<SM_ROW>(p, out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  if (mode == SM_E8M0) return launch_gemm_m<SM_E8M0>(p, out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  if (mode == SM_BLOCK) return launch_gemm_m<SM_BLOCK>(p, out_dt, qa, sa, qb, sb, M, N, K, c, s);
+  return launch_gemm_m<SM_TENSOR>(p, out_dt, qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace fp8amax

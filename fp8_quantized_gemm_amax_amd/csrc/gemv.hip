@@ -17,6 +17,7 @@
 // partial sums of C[m = l % 16][n = n0 + 16 j + 4 (l / 16) + r].  The waves' K shares are
 // summed in LDS and the epilogue scales and stores.
 #include "fp8_device.hpp"
+#include "gemm_plan.hpp"
 #include "launch.hpp"
 
 namespace fp8amax {
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
   const int iters = (count + UNROLL - 1) / UNROLL;
 
   // W rows n0 .. n0 + 16 NB - 1 and the M activation rows as buffers; a lane reads the
-  // 32 bytes of quarter kq of a slab in row r16 of a block.  The dispatcher keeps
-  // 16 NB K and M K below 2^31, so every offset fits the 32-bit buffer offset.
+  // 32 bytes of quarter kq of a slab in row r16 of a block.  plan_gemm keeps 16 NB K and
+  // 16 K below 2^31, so every offset fits the 32-bit buffer offset.
   const int rows = min(16 * NB, N - n0);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qb + static_cast<int64_t>(n0) * K), static_cast<short>(0), rows * K,
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
   const int nch = (K + 1023) / 1024;
   const int iters = (nch + UNROLL - 1) / UNROLL;
 
-  // RPW K and M K stay below 2^31 (the dispatcher checks 32 K), so offsets fit 32 bits
+  // RPW K and M K stay below 2^31 (plan_gemm checks 32 K), so offsets fit 32 bits
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qb + static_cast<int64_t>(row0) * K), static_cast<short>(0), rows * K,
       static_cast<int>(kRsrcWord3));
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(256) void gemv1_stream_kernel(
   const int KG = K / kSlab;                                   // blockwise: K % 128 == 0
   const int SR = E8M0 ? static_cast<int>(e8m0_row_bytes(KG)) : KG * 4;   // bytes per scale row
 
-  // N K < 2^31 (the dispatcher checks), so every offset fits 32 bits
+  // N K < 2^31 (plan_gemm checks), so every offset fits 32 bits
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(qb), static_cast<short>(0), N * K, static_cast<int>(kRsrcWord3));
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
@@ -497,82 +498,76 @@ __global__ __launch_bounds__(256) void gemv1_stream_kernel(
   }
 }
 
-constexpr int kStreamPerCu = 24;             // waves per CU of the persistent one-token kernel
-
 template <int BW, int OUT, int NCH>
-void launch_stream1_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int N, int K,
-                      void* c, hipStream_t s, int per_cu) {
-  const int waves = min(N, 256 * per_cu);
-  gemv1_stream_kernel<BW, OUT, NCH><<<(waves + 3) / 4, 256, 0, s>>>(qa, sa, qb, sb, N, K,
-                                                                    static_cast<uint16_t*>(c), waves);
+void launch_stream1_t(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                      const void* sb, int N, int K, void* c, hipStream_t s) {
+  const int waves = min(N, 256 * plan::kStreamPerCu);
+  gemv1_stream_kernel<BW, OUT, NCH><<<static_cast<unsigned>(L.grid), 256, 0, s>>>(qa, sa, qb, sb, N, K,
+                                                                                 static_cast<uint16_t*>(c), waves);
 }
 
 template <int BW, int OUT, int MT, int RPW, int UNROLL>
-void launch_valu_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-                   int K, void* c, hipStream_t s) {
-  const int waves = (N + RPW - 1) / RPW;
-  gemv_valu_kernel<BW, OUT, MT, RPW, UNROLL><<<(waves + 3) / 4, 256, 0, s>>>(
+void launch_valu_t(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                   const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  gemv_valu_kernel<BW, OUT, MT, RPW, UNROLL><<<static_cast<unsigned>(L.grid), 256, 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
 }
 
 template <int BW, int OUT, int WAVES, int UNROLL, int NB, int MB = 1>
-void launch_t(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-              int K, void* c, hipStream_t s) {
-  gemv_fp8_kernel<BW, OUT, WAVES, UNROLL, NB, MB><<<(N + 16 * NB - 1) / (16 * NB), WAVES * 64, 0, s>>>(
+void launch_t(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb,
+              int M, int N, int K, void* c, hipStream_t s) {
+  gemv_fp8_kernel<BW, OUT, WAVES, UNROLL, NB, MB><<<static_cast<unsigned>(L.grid), WAVES * 64, 0, s>>>(
       qa, sa, qb, sb, M, N, K, static_cast<uint16_t*>(c));
 }
 
-// Measured on MI355X with cold weights: one token runs best on the vector-ALU kernels
-// (1 KB row streams; one row per wave with four 1 KB loads in flight beat two or more rows
-// per wave by 5% at W[11008, 4096] and tied at W[18432, 7168]).  With float32 block scales
-// the persistent kernel with the activation row held in registers is 10-12% faster on both
-// shapes (24 waves per CU led 16 and 32); per tensor and with UE8M0 scales the one-wave-per-
-// row kernel stays ahead.  From two tokens on the MFMA kernel, with two row blocks per wave
-// once the activation fragment is worth sharing (M > 4).
+// Carries out a decode launch of a plan (plan_gemm in gemm_plan.hpp picks the kernel and
+// says why).  The persistent one-token kernel exists for float32 block scales only.
 template <int BW, int OUT>
-void launch_m(const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M, int N,
-              int K, void* c, hipStream_t s) {
-  if constexpr (BW == SM_BLOCK) {
-    if (M == 1 && K <= 8192 && static_cast<int64_t>(N) * K < (int64_t{1} << 31)) {
-      switch ((K + 1023) / 1024) {
-        case 1: launch_stream1_t<BW, OUT, 1>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        case 2: launch_stream1_t<BW, OUT, 2>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        case 3: launch_stream1_t<BW, OUT, 3>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        case 4: launch_stream1_t<BW, OUT, 4>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        case 5: launch_stream1_t<BW, OUT, 5>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        case 6: launch_stream1_t<BW, OUT, 6>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        case 7: launch_stream1_t<BW, OUT, 7>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
-        default: launch_stream1_t<BW, OUT, 8>(qa, sa, qb, sb, N, K, c, s, kStreamPerCu); break;
+bool launch_m(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb,
+              int M, int N, int K, void* c, hipStream_t s) {
+  switch (L.kernel) {
+    case FP8_KERNEL_GEMV_STREAM:
+      if constexpr (BW == SM_BLOCK) {
+        switch (L.variant) {
+          case 1: launch_stream1_t<BW, OUT, 1>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 2: launch_stream1_t<BW, OUT, 2>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 3: launch_stream1_t<BW, OUT, 3>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 4: launch_stream1_t<BW, OUT, 4>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 5: launch_stream1_t<BW, OUT, 5>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 6: launch_stream1_t<BW, OUT, 6>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 7: launch_stream1_t<BW, OUT, 7>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          case 8: launch_stream1_t<BW, OUT, 8>(L, qa, sa, qb, sb, N, K, c, s); return true;
+          default: return false;
+        }
       }
-      return;
-    }
+      return false;
+    case FP8_KERNEL_GEMV_VALU:
+      launch_valu_t<BW, OUT, 1, 1, 4>(L, qa, sa, qb, sb, M, N, K, c, s);
+      return true;
+    case FP8_KERNEL_GEMV_MFMA:
+      if (L.variant == 1) launch_t<BW, OUT, 2, 4, 1>(L, qa, sa, qb, sb, M, N, K, c, s);
+      else launch_t<BW, OUT, 4, 2, 2>(L, qa, sa, qb, sb, M, N, K, c, s);
+      return true;
+    default:
+      return false;
   }
-  if (M == 1) {
-    launch_valu_t<BW, OUT, 1, 1, 4>(qa, sa, qb, sb, M, N, K, c, s);
-  }
-  else if (M <= 4) launch_t<BW, OUT, 2, 4, 1>(qa, sa, qb, sb, M, N, K, c, s);
-  else launch_t<BW, OUT, 4, 2, 2>(qa, sa, qb, sb, M, N, K, c, s);
 }
 
 template <int SM>
-void launch_gemv_m(int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb, int M,
-                   int N, int K, void* c, hipStream_t s) {
-  if (out_dt == DT_BF16) launch_m<SM, DT_BF16>(qa, sa, qb, sb, M, N, K, c, s);
-  else launch_m<SM, DT_F16>(qa, sa, qb, sb, M, N, K, c, s);
+bool launch_gemv_m(int out_dt, const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, const uint8_t* qb,
+                   const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (out_dt == DT_BF16) return launch_m<SM, DT_BF16>(L, qa, sa, qb, sb, M, N, K, c, s);
+  return launch_m<SM, DT_F16>(L, qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace
 
-bool gemv_fits(int M, int K) {
-  return M >= 1 && M <= 16 && static_cast<int64_t>(K) * 32 < (int64_t{1} << 31);
-}
-
-void launch_gemv(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
-                 const void* sb, int M, int N, int K, void* c, hipStream_t s) {
-  if (mode == SM_ROW) launch_gemv_m<SM_ROW>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
-  else if (mode == SM_E8M0) launch_gemv_m<SM_E8M0>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
-  else if (mode == SM_BLOCK) launch_gemv_m<SM_BLOCK>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
-  else launch_gemv_m<SM_TENSOR>(out_dt, qa, sa, qb, sb, M, N, K, c, s);
+bool launch_gemv(int mode, int out_dt, const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa,
+                 const uint8_t* qb, const void* sb, int M, int N, int K, void* c, hipStream_t s) {
+  if (mode == SM_ROW) return launch_gemv_m<SM_ROW>(out_dt, L, qa, sa, qb, sb, M, N, K, c, s);
+  if (mode == SM_E8M0) return launch_gemv_m<SM_E8M0>(out_dt, L, qa, sa, qb, sb, M, N, K, c, s);
+  if (mode == SM_BLOCK) return launch_gemv_m<SM_BLOCK>(out_dt, L, qa, sa, qb, sb, M, N, K, c, s);
+  return launch_gemv_m<SM_TENSOR>(out_dt, L, qa, sa, qb, sb, M, N, K, c, s);
 }
 
 }  // namespace fp8amax

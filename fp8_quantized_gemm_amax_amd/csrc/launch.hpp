@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp8amax.h"
+
 namespace fp8amax {
 
 // How a GEMM is scaled (template argument of the GEMM kernels, argument of the launchers):
@@ -67,14 +69,14 @@ void launch_byte_mix(const void* x, int64_t n, uint8_t* q, hipStream_t s);
 bool launch_grouped(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb, const void* sb,
                     const int* offsets, int E, int T, int N, int K, void* c, hipStream_t s);
 
-// Decode GEMV path: whether it takes this shape (1 <= M <= 16, 32 K below 2^31) and its
-// launcher.  sa and sb point at float32 scales, or at e8m0fnu bytes for SM_E8M0.
-bool gemv_fits(int M, int K);
-void launch_gemv(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
-                 const void* sb, int M, int N, int K, void* c, hipStream_t s);
+// One decode launch of a plan (kernels FP8_KERNEL_GEMV_*).  sa and sb point at float32
+// scales, or at e8m0fnu bytes for SM_E8M0.  False for a launch it has no kernel for.
+bool launch_gemv(int mode, int out_dt, const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa,
+                 const uint8_t* qb, const void* sb, int M, int N, int K, void* c, hipStream_t s);
 
-// Scaled FP8 GEMM, C [M, N] of out_dt (dispatches M <= 16 to the GEMV path).
-void launch_gemm(int mode, int out_dt, const uint8_t* qa, const void* sa, const uint8_t* qb,
-                 const void* sb, int M, int N, int K, void* c, hipStream_t s);
+// Scaled FP8 GEMM, C [M, N] of out_dt: the launches of plan_gemm(mode, M, N, K), in order.
+// False (after the launches before it) for a launch it has no kernel for.
+bool launch_gemm(int mode, int out_dt, const fp8_gemm_plan_t& p, const uint8_t* qa, const void* sa,
+                 const uint8_t* qb, const void* sb, int M, int N, int K, void* c, hipStream_t s);
 
 }  // namespace fp8amax

@@ -117,6 +117,8 @@ fp8_status_t fp8_quantize_per_token_group(const void* x, fp8_dtype_t dt, int64_t
  * Products are accumulated in float32 on the gfx950 FP8 matrix cores.
  * Requires K % 16 == 0 (the task page pads hidden sizes to a multiple of 16) and K > 0.
  * M == 0 or N == 0 returns FP8_OK with nothing launched.
+ * Every GEMM entry point returns FP8_ERR_TOO_LARGE, before any HIP call, when M, N or K
+ * exceeds 2^31 - 1 or one of M K, N K, M N exceeds 2^40.
  */
 fp8_status_t fp8_gemm_scaled_tensorwise(const uint8_t* qa, const float* sa,
                                         const uint8_t* qb, const float* sb,
@@ -311,6 +313,63 @@ fp8_status_t fp8_debug_cast_f32(const float* v, uint8_t* q, int64_t n, void* str
  * FP8_ERR_MISALIGNED, all before any HIP call; n == 0 returns FP8_OK.
  */
 fp8_status_t fp8_debug_byte_mix(const void* x, uint8_t* q, int64_t n, void* stream);
+
+/*
+ * fp8_debug_gemm_plan - test hook: the kernel launches a scaled GEMM of this shape makes,
+ * computed by the same host code that the GEMM entry points run, without touching a GPU.
+ *   mode  : which GEMM (fp8_scale_mode_t below); M, N, K as in that entry point.
+ *   plan  : host pointer, filled on FP8_OK; plan->launches is 0 when M or N is 0.
+ * Each launch names its kernel, the output tile of one workgroup, the grid, the columns
+ * of C it writes, and two figures of its 32-bit buffer addressing: max_range, the largest
+ * byte range any of its buffer descriptors covers, and max_offset, the largest exclusive
+ * end of any byte offset it forms for a load of an element of one of its tiles (rows and
+ * columns past the operand's end included).  The kernels compute both in 32-bit signed
+ * arithmetic, so the dispatcher keeps them below 2^31.
+ * Errors: the shape errors of the GEMM entry point (FP8_ERR_BAD_SHAPE,
+ * FP8_ERR_TOO_LARGE) for that mode, FP8_ERR_BAD_SHAPE for an unknown mode, and
+ * FP8_ERR_NULL_POINTER for plan == NULL.
+ */
+typedef enum {
+  FP8_SCALE_TENSOR = 0,      /* fp8_gemm_scaled_tensorwise */
+  FP8_SCALE_BLOCK = 1,       /* fp8_gemm_scaled_blockwise */
+  FP8_SCALE_BLOCK_UE8M0 = 2, /* fp8_gemm_scaled_blockwise_ue8m0 */
+  FP8_SCALE_ROW = 3          /* fp8_gemm_scaled_rowwise */
+} fp8_scale_mode_t;
+
+typedef enum {
+  FP8_KERNEL_GEMV_STREAM = 1, /* one token, float32 block scales: persistent waves, one
+                                 weight row per wave at a time */
+  FP8_KERNEL_GEMV_VALU = 2,   /* one token: one weight row per wave on the vector ALUs */
+  FP8_KERNEL_GEMV_MFMA = 3,   /* 2-16 tokens on the matrix cores */
+  FP8_KERNEL_SKINNY = 4,      /* 17-128 tokens: weights streamed to registers, tokens in LDS */
+  FP8_KERNEL_TILE = 5,        /* tiled LDS-DMA kernel */
+  FP8_KERNEL_STAGED = 6       /* register-staged tiles with a zero-filled K tail */
+} fp8_gemm_kernel_t;
+
+typedef struct {
+  int32_t kernel;      /* fp8_gemm_kernel_t */
+  int32_t tile_m;      /* rows of C one workgroup covers (GEMV and SKINNY: all M rows) */
+  int32_t tile_n;      /* columns of C one workgroup covers per pass */
+  int32_t variant;     /* GEMV_STREAM: 1 KB chunks per row; GEMV_VALU: 1 KB loads in flight
+                          per wave; GEMV_MFMA: 16-row weight blocks per wave; SKINNY: 16-token
+                          blocks; TILE and STAGED: pipeline stages */
+  int32_t waves;       /* waves per workgroup (SKINNY: the compute waves, plus one loader) */
+  int32_t paired;      /* TILE: 1 if one wave of each SIMD pair issues the DMA for both */
+  int64_t grid;        /* workgroups launched */
+  int64_t threads;     /* threads per workgroup */
+  int64_t n_begin;     /* first column of C the launch writes */
+  int64_t n_end;       /* one past its last column */
+  int64_t max_range;   /* bytes */
+  int64_t max_offset;  /* bytes */
+} fp8_gemm_launch_t;
+
+typedef struct {
+  int32_t launches;    /* 0, 1 or 2, in the order they are enqueued */
+  int32_t reserved;
+  fp8_gemm_launch_t launch[2];
+} fp8_gemm_plan_t;
+
+fp8_status_t fp8_debug_gemm_plan(int32_t mode, int64_t M, int64_t N, int64_t K, fp8_gemm_plan_t* plan);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
                           "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
                           "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise",
                           "fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0",
-                          "fp8_debug_byte_mix"}
+                          "fp8_debug_byte_mix", "fp8_debug_gemm_plan"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
