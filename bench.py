@@ -61,6 +61,10 @@ def parse():
                    help="time only the workload's activation quantize (per token 1x128 groups or per "
                         "tensor) or its weight quantize (128x128 blocks), next to the byte-mix "
                         "reference (2 B read, 1 B written per element, no arithmetic) on the same tensors")
+    p.add_argument("--vendor-gemm", action="store_true",
+                   help="time the workload's GEMM (per tensor and per row/column scales) in this "
+                        "library and in the vendor FP8 GEMM behind torch._scaled_mm on the same codes "
+                        "and scales, cold inputs, HIP graphs; one JSON line")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the hot path, run a plain device copy of this many MiB "
                         "(the known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -264,6 +268,85 @@ def quantize_reference(args):
         "machine": machine_facts()}), flush=True)
 
 
+def vendor_reference(args):
+    """This library's per-tensor and per-row/column scaled GEMMs next to the vendor FP8 GEMM
+    (torch._scaled_mm, hipBLASLt on ROCm) on the workload's shape: the same codes and scales,
+    rotation sets of cold operands, each graph of R products replayed with events around it.
+    The two outputs are compared on the first set (a reference, not a parity test)."""
+    import torch
+    import fp8_quantized_gemm_amax_amd as fp8
+    from fp8_quantized_gemm_amax_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    M = args.m if args.m is not None else max(w.m_values)
+    N, K = w.n, w.k
+    a_bits, b_bits = wl.make_inputs(args.workload, M)
+    out_dtype = torch.float16 if w.out_dtype == "f16" else torch.bfloat16
+    a = wl.bits_to_tensor(a_bits, device=dev)
+    b = wl.bits_to_tensor(b_bits, device=dev)
+    qa, sa = fp8.fp8_quantize_per_tensor(a)
+    qb, sb = fp8.fp8_quantize_per_tensor(b)
+    ra, rsa = fp8.fp8_quantize_rowwise(a)
+    rb, rsb = fp8.fp8_quantize_rowwise(b)
+    del a, b
+    per_set = 2 * (M * K + N * K) + 2 * M * N
+    R = max(2, min(64, -(-ROTATION_BYTES // per_set)))
+    sets = [{"qa": qa.clone(), "qb": qb.clone(), "ra": ra.clone(), "rb": rb.clone(),
+             "c": torch.empty((M, N), dtype=out_dtype, device=dev)} for _ in range(R)]
+    e4m3 = torch.float8_e4m3fn
+    rsa2, rsb2 = rsa.reshape(M, 1), rsb.reshape(1, N)
+    legs = {
+        "ours_tensorwise": lambda x: fp8.fp8_gemm_scaled_tensorwise(x["qa"], sa, x["qb"], sb, out=x["c"]),
+        "vendor_tensorwise": lambda x: torch._scaled_mm(x["qa"].view(e4m3), x["qb"].view(e4m3).t(), scale_a=sa[0],
+                                                        scale_b=sb[0], out_dtype=out_dtype),
+        "ours_rowwise": lambda x: fp8.fp8_gemm_scaled_rowwise(x["ra"], rsa, x["rb"], rsb, out=x["c"]),
+        "vendor_rowwise": lambda x: torch._scaled_mm(x["ra"].view(e4m3), x["rb"].view(e4m3).t(), scale_a=rsa2,
+                                                     scale_b=rsb2, out_dtype=out_dtype),
+    }
+    flops = 2.0 * M * N * K
+    result = {}
+    for name, fn in legs.items():
+        try:
+            out = fn(sets[0]).float()
+            torch.cuda.synchronize()
+            for x in sets:
+                fn(x)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for x in sets:
+                    fn(x)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(3, -(-args.steps // R))
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for s0, s1 in ev:
+                s0.record()
+                g.replay()
+                s1.record()
+            torch.cuda.synchronize()
+            per = [s0.elapsed_time(s1) / R for s0, s1 in ev]
+            ms = sum(per) / len(per)
+            result[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                            "frac_of_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                            "us_dist": {k: round(v * 1e3, 2) for k, v in percentiles(per).items() if k != "n"},
+                            "_out": out}
+        except Exception as e:     # the vendor path may not exist for a dtype or shape
+            result[name] = {"error": repr(e)[:200]}
+    for kind in ("tensorwise", "rowwise"):
+        o, v = result.get("ours_" + kind, {}), result.get("vendor_" + kind, {})
+        if "_out" in o and "_out" in v:
+            d = (o["_out"] - v["_out"]).abs()
+            result[kind + "_max_rel_diff"] = round(float(d.max() / v["_out"].abs().max()), 6)
+    for r in result.values():
+        if isinstance(r, dict):
+            r.pop("_out", None)
+    print(json.dumps({"metric": "GEMM TFLOP/s, this library and the vendor FP8 GEMM",
+                      "config": {"workload": args.workload, "M": M, "N": N, "K": K, "rotation_sets": R,
+                                 "out": "f16" if out_dtype == torch.float16 else "bf16", "launch": "hip_graph"},
+                      **result, "machine": machine_facts()}), flush=True)
+
+
 def copy_reference(mib, steps):
     """A plain device copy of `mib` MiB, `steps` times (known bytes: mib MiB read + written)."""
     import torch
@@ -427,6 +510,9 @@ def main():
         return
     if args.quantize_only:
         quantize_reference(args)
+        return
+    if args.vendor_gemm:
+        vendor_reference(args)
         return
 
     import numpy as np

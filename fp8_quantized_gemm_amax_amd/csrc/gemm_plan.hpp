@@ -14,8 +14,8 @@
 namespace fp8amax {
 namespace plan {
 
-static_assert(FP8_SCALE_TENSOR == SM_TENSOR && FP8_SCALE_BLOCK == SM_BLOCK && FP8_SCALE_BLOCK_UE8M0 == SM_E8M0 &&
-                  FP8_SCALE_ROW == SM_ROW,
+static_assert(int{FP8_SCALE_TENSOR} == int{SM_TENSOR} && int{FP8_SCALE_BLOCK} == int{SM_BLOCK} &&
+                  int{FP8_SCALE_BLOCK_UE8M0} == int{SM_E8M0} && int{FP8_SCALE_ROW} == int{SM_ROW},
               "the C ABI's scale modes are the kernels' template values");
 
 constexpr int kCus = 256;              // compute units of one MI355X
