@@ -17,8 +17,8 @@
 //   gemm_dma_kernel: the tiled product for 129+ tokens.  A and B slabs move global -> LDS
 //     by LDS DMA into an NS-stage ring, eight (or four) waves multiply fragments read from
 //     LDS.  256x256 tiles when there is at least one per CU, launched as whole rounds plus
-//     a second launch of 256x128 tiles for a leftover half round; 128x128
-//     tiles otherwise.
+//     a second launch of 256x128 tiles for a leftover half round; 128x128 (or, without
+//     per-slab scales, 128x96) tiles otherwise.
 //   gemm_skinny_kernel / gemm_grouped_kernel: 17-128 tokens (and the mixture-of-experts
 //     chunks), weight rows streamed into registers, the tokens staged in LDS by one wave.
 //   gemm_fp8_kernel: K not a multiple of 128 (or too large for 32-bit buffer offsets),
@@ -904,6 +904,9 @@ bool run_launch(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, c
         launch_tile<256, 256, 64, 128, SM, OUT, 2, PAIR>(L, qa, sa, qb, sb, M, N, K, c, s);
       } else if (L.tile_m == 256) {
         launch_tile<256, 128, 64, 64, SM, OUT, 2, false>(L, qa, sa, qb, sb, M, N, K, c, s);
+      } else if (L.tile_n == 96) {
+        if constexpr (slab_scaled(SM)) return false;   // 48-column waves: no per-block scales
+        else launch_tile<128, 96, 64, 48, SM, OUT, 3, false>(L, qa, sa, qb, sb, M, N, K, c, s);
       } else if (L.waves == 4) {
         launch_tile<128, 128, 64, 64, SM, OUT, 2, false>(L, qa, sa, qb, sb, M, N, K, c, s);
       } else {

@@ -104,6 +104,10 @@ def check_plan(mode, M, N, K, plan):
             assert L["max_range"] >= min(bm, M) * K and L["max_range"] >= min(bn, n) * K
             if L["n_begin"] > 0:
                 assert L["n_begin"] % 128 == 0              # weight blocks and scales are plain offsets
+            if SLAB[mode]:
+                assert 128 % (bn // (L["waves"] // (bm // 64))) == 0   # a wave's columns in one weight block
+            if bn == 96:                                    # one round of them, where 128x128 is one round too
+                assert not SLAB[mode] and cdiv(M, 128) * cdiv(N, 96) <= 256 and cdiv(M, 128) * cdiv(N, 128) <= 256
         else:
             raise AssertionError(k)
 
@@ -127,7 +131,8 @@ def test_every_accepted_shape_has_a_plan_within_32_bit_addressing(mode):
     expect = {"gemv_valu", "gemv_mfma", "staged", "skinny", "tile"} | ({"gemv_stream"} if mode == "blockwise" else set())
     assert kinds == expect
     tiles = {(s[1], s[2], s[3]) for s in seen if s[0] == "tile"}
-    assert tiles == {(256, 256, 2), (256, 128, 2), (128, 128, 2), (128, 128, 3)}
+    assert tiles == {(256, 256, 2), (256, 128, 2), (128, 128, 2), (128, 128, 3)} | (
+        set() if SLAB[mode] else {(128, 96, 3)})
     assert {(s[1], s[2]) for s in seen if s[0] == "staged"} == {(16, 256), (128, 128)}
     assert {s[3] for s in seen if s[0] == "skinny"} == {2, 4, 8}
     assert {s[3] for s in seen if s[0] == "gemv_mfma"} == {1, 2}
@@ -159,7 +164,9 @@ def test_workload_kernels():
     def kinds(mode, M, N, K):
         return [(L["kernel"], L["tile_m"], L["tile_n"]) for L in fp8.fp8_debug_gemm_plan(mode, M, N, K)]
     assert kinds("tensorwise", 16, 64, 128) == [("gemv_mfma", 16, 32)]
-    assert kinds("tensorwise", 512, 5632, 2048) == [("tile", 128, 128)]
+    assert kinds("tensorwise", 512, 5632, 2048) == [("tile", 128, 96)]
+    assert kinds("rowwise", 512, 5632, 2048) == [("tile", 128, 96)]
+    assert kinds("blockwise", 512, 5632, 2048) == [("tile", 128, 128)]
     assert kinds("tensorwise", 1, 11008, 4096) == [("gemv_valu", 1, 1)]
     assert kinds("tensorwise", 128, 11008, 4096) == [("skinny", 128, 48)]
     assert kinds("blockwise", 1, 18432, 7168) == [("gemv_stream", 1, 1)]
