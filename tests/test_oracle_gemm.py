@@ -141,36 +141,33 @@ def test_check_gemm_inside_and_outside_bound():
     assert not oracle.check_gemm(nan, c, bnd, "bf16")["ok"]
 
 
-def pages_mechanism_torch(a, b, out_dtype):
-    """The Transformer Engine page's §3 mechanism, written with torch (float32
-    arithmetic, torch's float8_e4m3fn cast and float32 matmul)."""
-    def quant(x):
-        x = x.float()
-        s = x.abs().max() / 448.0
-        return (x / s).to(torch.float8_e4m3fn), s
-    qa, sa = quant(a)
-    qb, sb = quant(b)
-    acc = qa.float() @ qb.float().T
-    return qa, sa, qb, sb, (acc * sa * sb).to(out_dtype)
-
-
 @pytest.mark.parametrize("name", ["pertensor_16x64x128", "tinyllama_upproj_prefill"])
-def test_oracle_vs_pages_mechanism_in_torch(name):
+def test_oracle_against_torch_e4m3_cast_and_matmul(name):
+    """An independent cross-check of the per-tensor path: the oracle's amax and scale (its
+    own API) fed to torch's float8_e4m3fn conversion give the oracle's codes byte for byte,
+    and torch's float64 matmul of the decoded codes, times both scales, is the oracle's
+    exact product (so a dropped scale or a transposed operand in either would show)."""
     w = wl.WORKLOADS[name]
     a_bits, b_bits = wl.make_inputs(name)
-    a = wl.bits_to_tensor(a_bits)
-    b = wl.bits_to_tensor(b_bits)
-    tdt = torch.float16 if w.out_dtype == "f16" else torch.bfloat16
-    tqa, tsa, tqb, tsb, tc = pages_mechanism_torch(a, b, tdt)
     qa, sa = oracle.quantize_per_tensor(a_bits, "bf16")
     qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
-    # same fp32 arithmetic and the same round-to-nearest-even cast: identical bytes and scales
-    assert np.float32(tsa.item()) == sa and np.float32(tsb.item()) == sb
-    assert np.array_equal(tqa.view(torch.uint8).numpy(), qa)
-    assert np.array_equal(tqb.view(torch.uint8).numpy(), qb)
+    for bits, q, s in ((a_bits, qa, sa), (b_bits, qb, sb)):
+        x32 = oracle.input_to_f32(bits, "bf16")
+        scale = oracle.scale_from_amax(oracle.amax_per_tensor(x32))
+        assert np.float32(scale) == s
+        # float32 quotient (IEEE division in torch), then torch's round-to-nearest-even cast;
+        # nothing here saturates, since |x| / scale <= 448
+        t = (torch.from_numpy(x32) / torch.tensor(np.float32(scale))).to(torch.float8_e4m3fn)
+        assert np.array_equal(t.view(torch.uint8).numpy(), q)
+    da = torch.from_numpy(oracle.decode_e4m3(qa).astype(np.float64))
+    db = torch.from_numpy(oracle.decode_e4m3(qb).astype(np.float64))
+    c_torch = (da @ db.T).numpy() * (np.float64(sa) * np.float64(sb))
     c64 = oracle.gemm_tensorwise_ref(qa, sa, qb, sb)
+    # exact products of 3-bit mantissas summed in float64: equal up to summation order
     bnd = oracle.bound_tensorwise(qa, sa, qb, sb)
-    r = oracle.check_gemm(tc.double().numpy(), c64, bnd, w.out_dtype)
+    assert np.all(np.abs(c_torch - c64) <= 1e-12 * bnd + 1e-300)
+    tdt = torch.float16 if w.out_dtype == "f16" else torch.bfloat16
+    r = oracle.check_gemm(torch.from_numpy(c_torch).to(tdt).double().numpy(), c64, bnd, w.out_dtype)
     assert r["ok"], r
 
 
