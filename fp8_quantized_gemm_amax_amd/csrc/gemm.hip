@@ -409,11 +409,34 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   FragFactors<SM, TM, TN> ff;
   ff.load(sa, sb, m0 + wm * WM, wave_n0, M, N);
 
+  // Weight-block scales of this wave's block row nb: a window of 64 slabs (float32) or of
+  // 64 words of four UE8M0 bytes (256 slabs), lane l holding entry l, read per slab with
+  // readlane.  A per-slab scalar load would be waited for with lgkmcnt, the counter the
+  // slab's LDS fragment reads use, so every fragment wait after it would wait for it too.
+  // The window is loaded before the tile's first DMA and waited for there (vmcnt 0, which
+  // also tells the compiler's own wait insertion that it has arrived); a K of more than
+  // one window reloads it the same way at the window's first slab.
+  constexpr int kWin = E8M0 ? 256 : 64;
+  auto load_window = [&](int s0) -> uint32_t {
+    if constexpr (E8M0) {
+      const int word = s0 / 4 + lane;
+      return word < KG4 / 4 ? *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(sb_) +
+                                                                 static_cast<int64_t>(nb) * KG4 + 4 * word)
+                            : 0u;
+    } else {
+      const int g = s0 + lane;
+      return g < KG ? __float_as_uint(sb[static_cast<int64_t>(nb) * KG + g]) : 0u;
+    }
+  };
+  uint32_t sbw = 0;
+  if constexpr (BLOCKWISE) sbw = load_window(0);
+
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (BLOCKWISE) wait_vmcnt<0>();
 
   auto compute = [&](int s, int st) {
     const uint8_t* As = Abuf[st];
@@ -421,15 +444,14 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     float scl[TM];
     int ea[TM], eb = 127;
     if constexpr (E8M0) {
-      // the weight block's word is wave-uniform (a scalar load); each lane's activation
-      // word came with the slab's DMA
-      eb = e8m0_byte(*reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(sb_) +
-                                                         static_cast<int64_t>(nb) * KG4 + (s & ~3)), s);
+      // the weight block's word from the window; each lane's activation word came with
+      // the slab's DMA
+      eb = e8m0_byte(__builtin_amdgcn_readlane(sbw, (s % kWin) / 4), s);
       const float* Ss = Sbuf[st];
 #pragma unroll
       for (int i = 0; i < TM; ++i) ea[i] = e8m0_byte(__float_as_uint(Ss[w * WM + 16 * i + r16]), s);
     } else if constexpr (BLOCKWISE) {
-      const float sbv = sb[static_cast<int64_t>(nb) * KG + s];
+      const float sbv = __uint_as_float(__builtin_amdgcn_readlane(sbw, s % kWin));
       const float* Ss = Sbuf[st];
 #pragma unroll
       for (int i = 0; i < TM; ++i) scl[i] = Ss[w * WM + 16 * i + r16] * sbv;
@@ -466,6 +488,12 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   for (int p = 0; p < NS - 1; ++p)
     if (p < nslabs) issue(p, p);
   for (int s = 0; s < nslabs; ++s) {
+    if constexpr (BLOCKWISE) {
+      if (s > 0 && s % kWin == 0) {                    // the next window of weight-block scales
+        sbw = load_window(s);
+        wait_vmcnt<0>();
+      }
+    }
     const int ahead = min(NS - 2, nslabs - 1 - s);    // later slabs allowed to stay in flight
     if constexpr (PAIR) {
       if (lead) wait_slabs_ahead<2 * PER_SLAB, NS - 2>(ahead);
