@@ -187,6 +187,14 @@ __device__ __forceinline__ uint32_t max16(uint32_t v) {
   return v;
 }
 
+// Max over each aligned group of 8 lanes (the first three steps of max16).
+__device__ __forceinline__ uint32_t max8(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));   // row_half_mirror
+  return v;
+}
+
 // Max over the whole wave (64 lanes); every lane gets the result.
 __device__ __forceinline__ uint32_t max64(uint32_t v) {
   v = max16(v);

@@ -157,6 +157,48 @@ __global__ __launch_bounds__(kThreads) void group_1x128_vec_kernel(
   }
 }
 
+// Rows of whole groups (cols % 128 == 0): the groups are contiguous in memory, group g at
+// x + 128 g, so the tensor is one flat run of groups.  Eight lanes own a group, sixteen
+// elements (two 16-byte loads, one 16-byte store) each, and a wave takes eight consecutive
+// groups per step: its two load instructions cover one contiguous 2 KB piece and its store
+// 1 KB.  Against sixteen lanes of eight elements, the group's scale, reciprocal and lane
+// reduction are paid once per sixteen elements of a lane instead of eight.  Measured on
+// MI355X (A[4096, 7168] and A[4096, 4096], cold): 17.2 and 11.6 us against 19.0 and
+// 12.1 us for sixteen lanes per group, and 17.1 and 11.7 us for the byte-mix reference
+// (the same bytes moved with no arithmetic); two steps in flight per wave were no faster.
+template <int DT, bool WRITE_Q, bool E8M0 = false>
+__global__ __launch_bounds__(kThreads) void group_1x128_flat_kernel(
+    const uint16_t* __restrict__ x, int64_t ngroups, int64_t gcols, uint8_t* __restrict__ q,
+    void* __restrict__ out, int64_t sstride) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 7;                                   // lane within the group
+  const int gw = lane >> 3;                                   // group within the wave's step
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  const int64_t waves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  const int64_t wsteps = (ngroups + 7) >> 3;                  // steps of eight groups
+  for (int64_t i = wave; i < wsteps; i += waves) {
+    const int64_t g = (i << 3) + gw;
+    if (g >= ngroups) continue;                               // uniform within the group's lanes
+    const uint16_t* xg = x + (g << 7) + (sub << 4);
+    const U4 v0 = load16(xg), v1 = load16(xg + 8);
+    const float amax = amax_from_key<DT>(max8(max(key8(v0), key8(v1))));
+    if constexpr (WRITE_Q) {
+      const GroupScale<E8M0> gs(amax);
+      const float scale = gs.scale;
+      const bool fast = fast_scale(scale);
+      const float r = 1.0f / scale;
+      const uint2 a = enc8<DT>(v0, scale, r, fast), b = enc8<DT>(v1, scale, r, fast);
+      *reinterpret_cast<uint4*>(q + (g << 7) + (sub << 4)) = make_uint4(a.x, a.y, b.x, b.y);
+      if (sub == 0) {
+        const int64_t row = g / gcols;
+        gs.store(out, row, g - row * gcols, gcols, sstride);
+      }
+    } else {
+      if (sub == 0) static_cast<float*>(out)[g] = amax;
+    }
+  }
+}
+
 // Scalar path for rows whose length is not a multiple of 8: one group per 16-lane set.
 template <int DT, bool WRITE_Q, bool E8M0 = false>
 __global__ __launch_bounds__(kThreads) void group_1x128_scalar_kernel(
@@ -853,7 +895,12 @@ void launch_groups_t(const void* x, int64_t rows, int64_t cols, int32_t group_ro
   if (group_rows == 1) {
     const int64_t gcols = (cols + 127) / 128;
     const int64_t ngroups = rows * gcols;
-    if (vec) {
+    if (cols % 128 == 0) {
+      // 4096 elements per workgroup step, at most 32 workgroups per CU
+      const unsigned grid = grid_for(ngroups * 128, kThreads * 16, 256 * 32);
+      if (write_q) group_1x128_flat_kernel<DT, true, E8M0><<<grid, kThreads, 0, s>>>(xp, ngroups, gcols, q, out, sstride);
+      else group_1x128_flat_kernel<DT, false><<<grid, kThreads, 0, s>>>(xp, ngroups, gcols, q, out, sstride);
+    } else if (vec) {
       if (write_q) launch_group_vec<DT, true, kGroupUnroll, E8M0>(xp, rows, cols, kGroupSetsPerCu, q, out, sstride, s);
       else launch_group_vec<DT, false, kGroupUnroll>(xp, rows, cols, kGroupSetsPerCu, q, out, sstride, s);
     } else {
