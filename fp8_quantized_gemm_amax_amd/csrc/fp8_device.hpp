@@ -195,6 +195,21 @@ __device__ __forceinline__ uint32_t max8(uint32_t v) {
   return v;
 }
 
+// Sum of v over the 64 lanes of the wave, the same value in every lane (wave-uniform): DPP
+// adds within each row of 16 lanes (quads, half-rows, rows), then the four row sums read
+// with readlane.  No LDS crossbar (ds_bpermute) round trips, which a __shfl_xor butterfly
+// would take at every step.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));    // quad_perm [1,0,3,2]
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));    // quad_perm [2,3,0,1]
+  v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));   // row_half_mirror
+  v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));   // row_mirror
+  // readlane moves 32-bit integers: the float travels as its bits
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
 // Max over the whole wave (64 lanes); every lane gets the result.
 __device__ __forceinline__ uint32_t max64(uint32_t v) {
   v = max16(v);

@@ -446,12 +446,12 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
     if constexpr (E8M0) {
       // the weight block's word from the window; each lane's activation word came with
       // the slab's DMA
-      eb = e8m0_byte(__builtin_amdgcn_readlane(sbw, (s % kWin) / 4), s);
+      eb = e8m0_byte(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sbw), (s % kWin) / 4)), s);
       const float* Ss = Sbuf[st];
 #pragma unroll
       for (int i = 0; i < TM; ++i) ea[i] = e8m0_byte(__float_as_uint(Ss[w * WM + 16 * i + r16]), s);
     } else if constexpr (BLOCKWISE) {
-      const float sbv = __uint_as_float(__builtin_amdgcn_readlane(sbw, s % kWin));
+      const float sbv = __int_as_float(__builtin_amdgcn_readlane(static_cast<int>(sbw), s % kWin));
       const float* Ss = Sbuf[st];
 #pragma unroll
       for (int i = 0; i < TM; ++i) scl[i] = Ss[w * WM + 16 * i + r16] * sbv;

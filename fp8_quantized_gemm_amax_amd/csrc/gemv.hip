@@ -246,9 +246,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
 // (every e4m3 value is an f16 normal) and multiplied with v_dot2c_f32_f16, which forms the
 // products exactly and accumulates in float32.  A lane's 16 K positions lie in one
 // 128-wide slab, so the blockwise scale sa[m, g] * sb[n / 128, g] is applied to each
-// lane's 16-term partial.  At the end the 64 lanes' partials of each (m, row) are summed by
-// a butterfly.  The float32 sum is ordered differently from the MFMA path; both are within
-// the product tolerance of the exact sum.
+// lane's 16-term partial.  At the end the 64 lanes' partials of each (m, row) are summed
+// with DPP within rows of 16 lanes and readlane across them (wave_sum).  The float32 sum is
+// ordered differently from the MFMA path; both are within the product tolerance of the
+// exact sum.
 template <int SM, int OUT, int MT, int RPW, int UNROLL>
 __global__ __launch_bounds__(256) void gemv_valu_kernel(
     const uint8_t* __restrict__ qa, const void* __restrict__ sa_, const uint8_t* __restrict__ qb,
@@ -381,13 +382,11 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) consume(u);
 
-  // butterfly sum over the 64 lanes; every lane ends with every total
+  // sum over the 64 lanes; every lane ends with every total
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc[m][r] += __shfl_xor(acc[m][r], o, 64);
+    for (int r = 0; r < RPW; ++r) acc[m][r] = wave_sum(acc[m][r]);
 
   float alpha = 1.0f;
   if constexpr (SM == SM_TENSOR) alpha = sa[0] * sb[0];
@@ -491,8 +490,7 @@ __global__ __launch_bounds__(256) void gemv1_stream_kernel(
       fetch(row + waves, ch);                                  // the same chunk of the next row
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    acc = wave_sum(acc);
     const float f = SM == SM_ROW ? a_row * sb[row] : alpha;
     if (lane == 0) c[row] = static_cast<uint16_t>(f32_to_out_bits<OUT>(acc * f));
   }
