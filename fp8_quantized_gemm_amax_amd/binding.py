@@ -12,7 +12,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfp8amax.so")
+# FP8AMAX_LIBRARY selects another build of the same library (the tests load a host-sanitized
+# build of the argument checks this way); by default the in-tree build.
+LIB_PATH = os.environ.get("FP8AMAX_LIBRARY") or os.path.join(_PKG, "libfp8amax.so")
 
 FP8_BF16, FP8_F16 = 0, 1
 STATUS_NAMES = {0: "FP8_OK", 1: "FP8_ERR_NULL_POINTER", 2: "FP8_ERR_BAD_SHAPE", 3: "FP8_ERR_BAD_DTYPE",

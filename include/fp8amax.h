@@ -48,7 +48,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are 32-bit integers on both sides of the ABI.  A C++ translation unit
+ * gives them int32_t as fixed underlying type, so that any value a C caller passes (an
+ * unknown dtype, say, which the checks then reject) is a valid value of the type there
+ * too; C sees plain enums of the same size. */
+#ifdef __cplusplus
+#define FP8_ENUM_BASE : int32_t
+#else
+#define FP8_ENUM_BASE
+#endif
+
+typedef enum FP8_ENUM_BASE {
   FP8_OK = 0,
   FP8_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   FP8_ERR_BAD_SHAPE = 2,    /* negative size, unsupported group/block shape, K rule broken */
@@ -59,7 +69,7 @@ typedef enum {
 } fp8_status_t;
 
 /* 16-bit floating point types used for inputs (activations, weights) and outputs. */
-typedef enum { FP8_BF16 = 0, FP8_F16 = 1 } fp8_dtype_t;
+typedef enum FP8_ENUM_BASE { FP8_BF16 = 0, FP8_F16 = 1 } fp8_dtype_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8_status_string(fp8_status_t s);
@@ -329,14 +339,14 @@ fp8_status_t fp8_debug_byte_mix(const void* x, uint8_t* q, int64_t n, void* stre
  * FP8_ERR_TOO_LARGE) for that mode, FP8_ERR_BAD_SHAPE for an unknown mode, and
  * FP8_ERR_NULL_POINTER for plan == NULL.
  */
-typedef enum {
+typedef enum FP8_ENUM_BASE {
   FP8_SCALE_TENSOR = 0,      /* fp8_gemm_scaled_tensorwise */
   FP8_SCALE_BLOCK = 1,       /* fp8_gemm_scaled_blockwise */
   FP8_SCALE_BLOCK_UE8M0 = 2, /* fp8_gemm_scaled_blockwise_ue8m0 */
   FP8_SCALE_ROW = 3          /* fp8_gemm_scaled_rowwise */
 } fp8_scale_mode_t;
 
-typedef enum {
+typedef enum FP8_ENUM_BASE {
   FP8_KERNEL_GEMV_STREAM = 1, /* one token, float32 block scales: persistent waves, one
                                  weight row per wave at a time */
   FP8_KERNEL_GEMV_VALU = 2,   /* one token: one weight row per wave on the vector ALUs */
