@@ -400,11 +400,13 @@ def algorithmic_bytes(w, M, scheme="tensorwise"):
     return quant_a + gemm + quant_b, gemm
 
 
-def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
+def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise", gpu_c=None):
     """The oracle's quantize(A) + scaled GEMM on the host, on a row sample of A sized to
     roughly `budget_s` seconds; returns TFLOP/s (float64 arithmetic).  With delayed
     scaling the step is the oracle's static cast with the history's scale, its history
-    update, and the GEMM."""
+    update, and the GEMM.  With `gpu_c` (the GPU step's output for the same inputs) the
+    sampled rows of it are also checked against the oracle's, outside the timing, with the
+    product tolerance."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
@@ -437,24 +439,24 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
             qa, sa = oracle.quantize_rowwise(a, "bf16")
             if w.quantize_b_per_call:
                 qb, sb = oracle.quantize_rowwise(b_bits, "bf16")
-            oracle.gemm_rowwise_ref(qa, sa, qb, sb)
+            c_or = oracle.gemm_rowwise_ref(qa, sa, qb, sb)
         elif delayed:
             qa, amax = oracle.quantize_static(a, "bf16", scale_a)
             oracle.delayed_step(hist, step_a, scale_a, amax, DELAYED_INTERVAL, DELAYED_MARGIN)
             if w.quantize_b_per_call:
                 qb, _ = oracle.quantize_static(b_bits, "bf16", sb)
-            oracle.gemm_tensorwise_ref(qa, scale_a, qb, sb)
+            c_or = oracle.gemm_tensorwise_ref(qa, scale_a, qb, sb)
         elif w.mode == "tensorwise":
             qa, sa = oracle.quantize_per_tensor(a, "bf16")
             if w.quantize_b_per_call:
                 qb, sb = oracle.quantize_per_tensor(b_bits, "bf16")
-            oracle.gemm_tensorwise_ref(qa, sa, qb, sb)
+            c_or = oracle.gemm_tensorwise_ref(qa, sa, qb, sb)
         elif ue8m0:
             qa, sa = oracle.quantize_groups_ue8m0(a, "bf16", 1, 128)
-            oracle.gemm_blockwise_ue8m0_ref(qa, sa, qb, sb)
+            c_or = oracle.gemm_blockwise_ue8m0_ref(qa, sa, qb, sb)
         else:
             qa, sa = oracle.quantize_groups(a, "bf16", 1, 128)
-            oracle.gemm_blockwise_ref(qa, sa, qb, sb)
+            c_or = oracle.gemm_blockwise_ref(qa, sa, qb, sb)
         dt = time.perf_counter() - t0
         runs.append(dt)
         if len(runs) == 1 and (dt * 3 > budget_s and rows > 1 or dt * 3 < 0.5 * budget_s and rows < M):
@@ -465,10 +467,31 @@ def cpu_baseline(w, a_bits, b_bits, budget_s=20.0, scheme="tensorwise"):
             break
     best = min(runs)
     flops = 2.0 * rows * N * K
-    return {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle {'delayed-scaling ' if delayed else ''}quantize(A[{rows},{K}]) + "
-                      f"{scheme} GEMM with W[{N},{K}], best of "
-                      f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
+    out = {"value": round(flops / best / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"oracle {'delayed-scaling ' if delayed else ''}quantize(A[{rows},{K}]) + "
+                     f"{scheme} GEMM with W[{N},{K}], best of "
+                     f"{len(runs)} ({best:.2f} s); float64 NumPy, {cores} host threads"}
+    if gpu_c is not None:
+        if scheme == "rowwise":
+            bnd = oracle.bound_rowwise(qa, sa, qb, sb)
+        elif delayed:
+            bnd = oracle.bound_tensorwise(qa, scale_a, qb, sb)
+        elif w.mode == "tensorwise":
+            # the GPU's activation scale comes from the whole A: quantize the sample with it
+            sa = np.float32(oracle.scale_from_amax(oracle.amax_per_tensor(oracle.input_to_f32(a_bits, "bf16"))))
+            qa = oracle.quantize_with_scale(oracle.input_to_f32(a_bits[:rows], "bf16"), sa)
+            c_or = oracle.gemm_tensorwise_ref(qa, sa, qb, sb)
+            bnd = oracle.bound_tensorwise(qa, sa, qb, sb)
+        elif ue8m0:
+            bnd = oracle.bound_blockwise_ue8m0(qa, sa, qb, sb)
+        else:
+            bnd = oracle.bound_blockwise(qa, sa, qb, sb)
+        got = gpu_c[:rows].float().cpu().numpy().astype(np.float64)
+        r = oracle.check_gemm(got, c_or, bnd, w.out_dtype)
+        out["check"] = {"rows": rows, "ok": bool(r["ok"]), "n_bad": int(r["n_bad"]),
+                        "worst_ratio": round(float(r["worst_ratio"]), 4),
+                        "tolerance": "2e-3 |C| + 1e-4 sum|qa sa||qb sb| + one output ulp"}
+    return out
 
 
 def cpu_baseline_grouped(w, a_bits, scheme, cores):
@@ -768,7 +791,7 @@ def main():
                                  "rows_per_expert_max": int(sizes.max())})
     result["machine"] = machine_facts()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scheme=scheme)
+        result["cpu_baseline"] = cpu_baseline(w, a_bits, b_bits, scheme=scheme, gpu_c=None if grouped else ref_c)
     print(json.dumps(result), flush=True)
 
 
