@@ -47,6 +47,7 @@ _SIGNATURES = {
     "fp8_debug_cast_f32": ([_P, _P, _I64, _P], ctypes.c_int),
     "fp8_debug_byte_mix": ([_P, _P, _I64, _P], ctypes.c_int),
     "fp8_debug_gemm_plan": ([_I32, _I64, _I64, _I64, _P], ctypes.c_int),
+    "fp8_gemv_dynamic": ([_I32, _P, ctypes.c_int, _P, _P, _I64, _I64, _P, _P, _P, ctypes.c_int, _P], ctypes.c_int),
 }
 
 
@@ -513,3 +514,65 @@ def fp8_debug_gemm_plan(mode, M, N, K):
         d["kernel"] = GEMM_KERNELS[l.kernel]
         out.append(d)
     return out
+
+
+def _act_scale_spec(mode, K):
+    """Shape and dtype of the activation scales fp8_gemv_dynamic writes for x as [1, K]: those
+    of the quantizer that pairs with `mode`."""
+    if mode in ("tensorwise", "rowwise"):
+        return (1,), torch.float32
+    if mode == "blockwise":
+        return (1, K // 128), torch.float32
+    return (1, e8m0_row_bytes(K // 128)), torch.uint8
+
+
+def _weight_scale_spec(mode, N, K):
+    """Shape and dtype of the weight scales the GEMM of `mode` takes for qb [N, K]."""
+    if mode == "tensorwise":
+        return (1,), torch.float32
+    if mode == "rowwise":
+        return (N,), torch.float32
+    if mode == "blockwise":
+        return (-(-N // 128), K // 128), torch.float32
+    return (-(-N // 128), e8m0_row_bytes(K // 128)), torch.uint8
+
+
+def fp8_gemv_dynamic(mode, x, qb, sb, out_dtype=torch.bfloat16, out=None, qa=None, sa=None):
+    """The whole one-token step in one call: x ([K] or [1, K], bf16/fp16) quantized with the
+    scheme that pairs with `mode` ("tensorwise": one scale; "rowwise": the row's scale;
+    "blockwise": 1x128 groups with float32 scales; "blockwise_ue8m0": 1x128 groups with UE8M0
+    scales), then multiplied with qb [N, K] and its scales sb as the GEMM of that mode takes
+    them.  Returns (out [1, N], qa uint8 [1, K], sa), qa and sa as the matching quantizer
+    writes them for x as [1, K]."""
+    if mode not in GEMM_MODES:
+        raise ValueError(f"mode must be one of {sorted(GEMM_MODES)}, got {mode!r}")
+    if x.dim() == 1:
+        x = x.reshape(1, -1)
+    x = _as_2d(x)
+    if x.shape[0] != 1:
+        raise ValueError(f"one token: x must be [K] or [1, K], got {tuple(x.shape)}")
+    qb = _codes(_as_2d(qb))
+    _same_device(x, qb, sb)
+    K = x.shape[1]
+    N, K2 = qb.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: x has {K}, qb has {K2}")
+    sb = sb.contiguous()
+    if K > 0 and (K % 128 == 0 or mode in ("tensorwise", "rowwise")):
+        shape, dtype = _weight_scale_spec(mode, N, K)
+        if tuple(sb.shape) != shape or sb.dtype != dtype:
+            raise ValueError(f"{mode} weight scales must be {dtype} {shape}, got {sb.dtype} {tuple(sb.shape)}")
+    a_shape, a_dtype = _act_scale_spec(mode, K)
+    if qa is None:
+        qa = torch.empty((1, K), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty(a_shape, dtype=a_dtype, device=x.device)
+    if out is None:
+        out = torch.empty((1, N), dtype=out_dtype, device=x.device)
+    _check_out(qa, (1, K), _CODES, "qa", x, (x, qb, sb))
+    _check_out(sa, a_shape, (a_dtype,), "sa", x, (x, qb, sb, qa))
+    _check_out(out, (1, N), _OUT, "out", x, (x, qb, sb, qa, sa))
+    _check("fp8_gemv_dynamic",
+           lib().fp8_gemv_dynamic(GEMM_MODES[mode], _ptr(x), _dt(x), _ptr(qb), _ptr(sb), N, K, _ptr(qa), _ptr(sa),
+                                  _ptr(out), _out_dt(out.dtype), _stream(x)))
+    return out, qa, sa

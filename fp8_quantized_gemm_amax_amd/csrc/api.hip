@@ -275,6 +275,35 @@ fp8_status_t fp8_debug_gemm_plan(int32_t mode, int64_t M, int64_t N, int64_t K, 
   return gemm_shape(mode, M, N, K, plan);
 }
 
+fp8_status_t fp8_gemv_dynamic(int32_t mode, const void* x, fp8_dtype_t in_dt, const uint8_t* qb, const void* sb,
+                              int64_t N, int64_t K, uint8_t* qa, void* sa, void* c, fp8_dtype_t out_dt,
+                              void* stream) {
+  if (mode < FP8_SCALE_TENSOR || mode > FP8_SCALE_ROW) return FP8_ERR_BAD_SHAPE;
+  fp8_gemm_plan_t plan;
+  const fp8_status_t st = gemm_shape(mode, 1, N, K, &plan);
+  if (st != FP8_OK) return st;
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return FP8_ERR_BAD_DTYPE;
+  if (!x || !qa || !sa || (N > 0 && (!qb || !sb || !c))) return FP8_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(qa) || !aligned4(sa) ||
+      (N > 0 && (!aligned16(qb) || !aligned4(sb) || !aligned16(c))))
+    return FP8_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int idt = static_cast<int>(in_dt), odt = static_cast<int>(out_dt);
+  (void)hipGetLastError();
+  if (fp8amax::plan::dynamic_fits(N, K)) {
+    fp8amax::launch_gemv_dynamic(mode, idt, odt, x, qb, sb, qa, sa, static_cast<int>(N), static_cast<int>(K), c, s);
+    return finish_launch();
+  }
+  // the quantizer of the mode, then the one-token GEMM
+  if (mode == FP8_SCALE_TENSOR) fp8amax::launch_tensor_quantize(idt, x, K, static_cast<float*>(sa), qa, s);
+  else if (mode == FP8_SCALE_ROW) fp8amax::launch_rows(idt, x, 1, K, qa, static_cast<float*>(sa), s);
+  else if (mode == FP8_SCALE_BLOCK) fp8amax::launch_groups(idt, x, 1, K, 1, qa, static_cast<float*>(sa), true, s);
+  else fp8amax::launch_groups_e8m0(idt, x, 1, K, 1, qa, static_cast<uint8_t*>(sa), s);
+  if (N > 0 && !fp8amax::launch_gemm(mode, odt, plan, qa, sa, qb, sb, 1, static_cast<int>(N), static_cast<int>(K), c, s))
+    return FP8_ERR_LAUNCH;
+  return finish_launch();
+}
+
 fp8_status_t fp8_debug_byte_mix(const void* x, uint8_t* q, int64_t n, void* stream) {
   if (n < 0) return FP8_ERR_BAD_SHAPE;
   if (n > kMaxElems) return FP8_ERR_TOO_LARGE;

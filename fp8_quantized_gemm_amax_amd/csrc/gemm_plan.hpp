@@ -37,6 +37,14 @@ inline int64_t scale_row_bytes(int sm, int64_t K) {
 // row block of the two-block MFMA variant) within 32-bit offsets.
 inline bool gemv_fits(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K * 32 <= kLimit32; }
 
+// Whether the fused one-token step (the activation row quantized and multiplied in one
+// launch) takes the shape: an eight-wave workgroup holds the row as one 1 KB chunk per wave,
+// so K <= 8192, and the weight rows are addressed with 32-bit buffer offsets, so N K < 2^31.
+constexpr int kDynWaves = 8;
+inline bool dynamic_fits(int64_t N, int64_t K) {
+  return N >= 1 && K >= 1 && K <= 1024 * kDynWaves && N * K <= kLimit32;
+}
+
 // Whether the LDS-DMA kernels take K: whole slabs, and 256 rows of K bytes (the largest
 // tile) within 32-bit offsets.  Other K go to the register-staged kernel.
 inline bool dma_fits(int64_t K) { return K % kSlabK == 0 && K * 256 <= kLimit32; }

@@ -74,6 +74,11 @@ bool launch_grouped(int mode, int out_dt, const uint8_t* qa, const void* sa, con
 bool launch_gemv(int mode, int out_dt, const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa,
                  const uint8_t* qb, const void* sb, int M, int N, int K, void* c, hipStream_t s);
 
+// The fused one-token step (plan::dynamic_fits(N, K)): x [K] quantized with the scheme of
+// `mode` into qa [K] and sa, and C [N] = the one-token GEMM of that mode, in one launch.
+void launch_gemv_dynamic(int mode, int in_dt, int out_dt, const void* x, const uint8_t* qb, const void* sb,
+                         uint8_t* qa, void* sa, int N, int K, void* c, hipStream_t s);
+
 // Scaled FP8 GEMM, C [M, N] of out_dt: the launches of plan_gemm(mode, M, N, K), in order.
 // False (after the launches before it) for a launch it has no kernel for.
 bool launch_gemm(int mode, int out_dt, const fp8_gemm_plan_t& p, const uint8_t* qa, const void* sa,

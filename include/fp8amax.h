@@ -381,6 +381,37 @@ typedef struct {
 
 fp8_status_t fp8_debug_gemm_plan(int32_t mode, int64_t M, int64_t N, int64_t K, fp8_gemm_plan_t* plan);
 
+/*
+ * fp8_gemv_dynamic - the whole step for one token, the batch-1 decode case: the interface
+ * of the Transformer Engine page's section 3 pseudocode (fp8_gemm takes the 16-bit operand,
+ * takes its amax, scales, casts, multiplies and rescales inside), with the weights already
+ * quantized, and with the dynamic activation scheme of the fine-grained FP8 page
+ * (activation_scheme "dynamic": the activation scales are taken from each call's input).
+ * The activation row x is quantized with the scheme that pairs with `mode`:
+ *   FP8_SCALE_TENSOR      : one scale, sa float32 [1] (fp8_quantize_per_tensor of x as [1, K]);
+ *   FP8_SCALE_ROW         : the row's scale, sa float32 [1] (fp8_quantize_rowwise of x as [1, K]);
+ *   FP8_SCALE_BLOCK       : 1 x 128 groups, sa float32 [K/128] (fp8_quantize_per_token_group);
+ *   FP8_SCALE_BLOCK_UE8M0 : 1 x 128 groups, sa uint8 e8m0fnu [G4], G4 = K/128 rounded up to a
+ *                           multiple of 4, padding bytes 127 (fp8_quantize_per_token_group_ue8m0);
+ * and its codes qa [K] and scales sa are written bit for bit as that quantizer writes them.
+ * Then c [N] = the GEMM of `mode` with M = 1: fp8_gemm_scaled_tensorwise, _rowwise,
+ * _blockwise or _blockwise_ue8m0 of (qa, sa) with (qb, sb), bit for bit.
+ *   mode : fp8_scale_mode_t.
+ *   x    : bf16/fp16 [K] (device), 16-byte aligned, of `in_dt`.
+ *   qb   : uint8 e4m3 [N, K] (device), 16-byte aligned; sb as the GEMM of `mode` takes it
+ *          (float32 [1], [N] or [ceil(N/128), K/128]; UE8M0 bytes [ceil(N/128), G4]).
+ *   qa   : uint8 output [K] (device), 16-byte aligned; sa: output as above, 4-byte aligned.
+ *   c    : bf16/fp16 output [N] of `out_dt` (device), 16-byte aligned.
+ * Requires K > 0 and K % 16 == 0 (K % 128 == 0 for the block modes).  With N >= 1, K <= 8192
+ * and N * K < 2^31 all of it is one launch; otherwise the quantizer's launches and then the
+ * GEMM's, with the same results.  N == 0 quantizes x only (c may be NULL).  x must not share
+ * memory with qa, sa or c.  Errors: FP8_ERR_BAD_SHAPE (an unknown mode, K rule, negative N),
+ * FP8_ERR_TOO_LARGE, FP8_ERR_BAD_DTYPE, FP8_ERR_NULL_POINTER, FP8_ERR_MISALIGNED, FP8_ERR_LAUNCH.
+ */
+fp8_status_t fp8_gemv_dynamic(int32_t mode, const void* x, fp8_dtype_t in_dt, const uint8_t* qb, const void* sb,
+                              int64_t N, int64_t K, uint8_t* qa, void* sa, void* c, fp8_dtype_t out_dt,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
                           "fp8_quantize_static", "fp8_delayed_scaling_update", "fp8_quantize_delayed",
                           "fp8_quantize_rowwise", "fp8_gemm_scaled_rowwise",
                           "fp8_gemm_grouped_blockwise", "fp8_gemm_grouped_blockwise_ue8m0",
-                          "fp8_debug_byte_mix", "fp8_debug_gemm_plan"}
+                          "fp8_debug_byte_mix", "fp8_debug_gemm_plan", "fp8_gemv_dynamic"}
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding._SIGNATURES)
@@ -194,6 +194,38 @@ def test_fused_delayed_validation(L):
     assert call(x=A16 + 4) == ALIGN
     assert call(step=A16 + 2) == ALIGN
     assert call(rows=0, x=MIS, q=MIS, used=A16 + 1) == ALIGN             # x, q unused when empty
+
+
+def test_gemv_dynamic_validation(L):
+    """fp8_gemv_dynamic(mode, x, in_dt, qb, sb, N, K, qa, sa, c, out_dt, stream): only failing
+    cases, and the argument order of their checks (mode, shape, dtype, pointers, alignment)."""
+    f = L.fp8_gemv_dynamic
+
+    def call(mode=0, x=A16, dt=0, qb=A16, sb=A16, N=64, K=256, qa=A16, sa=A16, c=A16, odt=0):
+        return f(mode, x, dt, qb, sb, N, K, qa, sa, c, odt, None)
+
+    assert call(mode=-1) == SHAPE
+    assert call(mode=4) == SHAPE
+    assert call(K=0) == SHAPE
+    assert call(K=24) == SHAPE                                        # K % 16
+    assert call(mode=1, K=1040) == SHAPE                              # blockwise: K % 128
+    assert call(mode=2, K=1040) == SHAPE
+    assert call(N=-1) == SHAPE
+    assert call(N=2 ** 31) == LARGE
+    assert call(dt=2) == DTYPE
+    assert call(odt=9) == DTYPE
+    assert call(x=None) == NULLP
+    assert call(qa=None) == NULLP
+    assert call(sa=None) == NULLP
+    assert call(qb=None) == NULLP
+    assert call(c=None) == NULLP
+    assert call(N=0, qb=None, sb=None, c=None, x=MIS) == ALIGN        # N == 0: x is still quantized
+    assert call(x=A16 + 8) == ALIGN
+    assert call(qa=MIS) == ALIGN
+    assert call(sa=A16 + 2) == ALIGN
+    assert call(c=MIS) == ALIGN
+    assert call(qb=MIS) == ALIGN
+    assert call(sb=A16 + 1) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -71,6 +71,20 @@ def test_check_out_rules():
                                            out=torch.empty((6, 9), dtype=torch.bfloat16)),
     lambda b: b.fp8_quantize_static(x16(4, 32), torch.ones(1), q=torch.empty((4, 31), dtype=torch.uint8)),
     lambda b: b.fp8_debug_cast_f32(torch.zeros(16), q=torch.empty(15, dtype=torch.uint8)),
+    lambda b: b.fp8_gemv_dynamic("tensorwise", x16(1, 256), torch.zeros((8, 256), dtype=torch.uint8), torch.ones(1),
+                                 out=torch.empty((8,), dtype=torch.bfloat16)),
+    lambda b: b.fp8_gemv_dynamic("blockwise", x16(1, 256), torch.zeros((8, 256), dtype=torch.uint8),
+                                 torch.ones((1, 2)), sa=torch.empty((1,), dtype=torch.float32)),
+    lambda b: b.fp8_gemv_dynamic("blockwise_ue8m0", x16(1, 256), torch.zeros((8, 256), dtype=torch.uint8),
+                                 torch.ones((1, 4), dtype=torch.uint8), sa=torch.empty((1, 2), dtype=torch.uint8)),
+    lambda b: b.fp8_gemv_dynamic("rowwise", x16(1, 256), torch.zeros((8, 256), dtype=torch.uint8), torch.ones(8),
+                                 qa=torch.empty((256,), dtype=torch.uint8)),
+    lambda b: b.fp8_gemv_dynamic("rowwise", x16(1, 256), torch.zeros((8, 256), dtype=torch.uint8),
+                                 torch.ones(1)),                                  # weight scales: [N]
+    lambda b: b.fp8_gemv_dynamic("blockwise", x16(2, 256), torch.zeros((8, 256), dtype=torch.uint8),
+                                 torch.ones((1, 2))),                             # one token only
+    lambda b: b.fp8_gemv_dynamic("per_tensor", x16(1, 256), torch.zeros((8, 256), dtype=torch.uint8),
+                                 torch.ones(1)),                                  # unknown mode
 ])
 def test_bad_outputs_rejected_before_the_library(cpu_binding, call):
     with pytest.raises((TypeError, ValueError)):
@@ -90,3 +104,13 @@ def test_gemm_out_must_not_overlap_operands(cpu_binding):
     with pytest.raises(ValueError, match="overlaps"):
         cpu_binding.fp8_gemm_scaled_tensorwise(qa, torch.ones(1), torch.zeros((8, 64), dtype=torch.uint8),
                                                torch.ones(1), out=qa.reshape(-1)[:64].view(torch.bfloat16).view(4, 8))
+
+
+def test_gemv_dynamic_outputs_must_not_overlap_x(cpu_binding):
+    """Every workgroup of the fused step reads x while the first one writes qa and sa."""
+    x = x16(1, 512)
+    qb = torch.zeros((8, 512), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="overlaps"):
+        cpu_binding.fp8_gemv_dynamic("tensorwise", x, qb, torch.ones(1), qa=x.view(torch.uint8)[:, :512])
+    with pytest.raises(ValueError, match="overlaps"):
+        cpu_binding.fp8_gemv_dynamic("tensorwise", x, qb, torch.ones(1), out=x[:, :8])
