@@ -65,15 +65,22 @@ def parse():
                    help="time the workload's GEMM (per tensor and per row/column scales) in this "
                         "library and in the vendor FP8 GEMM behind torch._scaled_mm on the same codes "
                         "and scales, cold inputs, HIP graphs; one JSON line")
+    p.add_argument("--two-launch", action="store_true",
+                   help="one token: time the quantize launch followed by the one-token GEMM instead "
+                        "of the fused step (fp8_gemv_dynamic, one launch)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the hot path, run a plain device copy of this many MiB "
                         "(the known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
 
 
-KERNEL_SOURCES = ["fp8_quantized_gemm_amax_amd/csrc/gemm.hip", "fp8_quantized_gemm_amax_amd/csrc/gemv.hip",
-                  "fp8_quantized_gemm_amax_amd/csrc/gemm_common.hpp", "fp8_quantized_gemm_amax_amd/csrc/dma.hpp",
-                  "fp8_quantized_gemm_amax_amd/csrc/fp8_device.hpp"]
+_CSRC = "fp8_quantized_gemm_amax_amd/csrc/"
+# the sources of each kernel family's code: the tiled and few-token GEMMs (M > 16), and the
+# decode kernels with the fused one-token step (M <= 16)
+KERNEL_SOURCES = {
+    "gemm": [_CSRC + f for f in ("gemm.hip", "gemm_common.hpp", "dma.hpp", "fp8_device.hpp", "gemm_plan.hpp")],
+    "decode": [_CSRC + f for f in ("gemv.hip", "fp8_device.hpp", "quant_device.hpp", "gemm_plan.hpp")],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -103,12 +110,12 @@ def strip_comments(src):
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash():
-    """Hash of the GEMM kernels' code (comments and layout excluded): the counter table's
-    entries hold only while it is unchanged."""
+def kernel_source_hash(M):
+    """Hash of the code of the kernel family that runs M tokens (comments and layout
+    excluded): the counter table's entries hold only while it is unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES["decode" if M <= 16 else "gemm"]:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(strip_comments(f.read()).encode())
         h.update(b"\0")
@@ -127,13 +134,14 @@ def scheme_of(w, scale_fmt="float32", act_scaling="dynamic", rowwise=False):
     return "blockwise-ue8m0" if scale_fmt == "ue8m0" else "blockwise"
 
 
-def traffic_key(workload, M, scheme="tensorwise"):
-    """Counter-table key of a GEMM launch (delayed scaling runs the tensorwise GEMM)."""
+def traffic_key(workload, M, scheme="tensorwise", fused=False):
+    """Counter-table key of a GEMM launch (delayed scaling runs the tensorwise GEMM; `fused`:
+    the one-token step's single launch)."""
     suffix = {"blockwise-ue8m0": "/ue8m0", "grouped-ue8m0": "/ue8m0", "rowwise": "/rowwise"}.get(scheme, "")
-    return f"{workload}/M={M}" + suffix
+    return f"{workload}/M={M}" + suffix + ("/fused" if fused else "")
 
 
-def measured_traffic(workload, M, scheme="tensorwise"):
+def measured_traffic(workload, M, scheme="tensorwise", fused=False):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, or None when
     there is no entry for this workload or the kernel sources changed since it was taken."""
     import json as _json
@@ -142,8 +150,8 @@ def measured_traffic(workload, M, scheme="tensorwise"):
             table = _json.load(f)
     except (OSError, ValueError):
         return None
-    e = table.get(traffic_key(workload, M, scheme))
-    if not e or e.get("kernel_source_sha") != kernel_source_hash():
+    e = table.get(traffic_key(workload, M, scheme, fused))
+    if not e or e.get("kernel_source_sha") != kernel_source_hash(M):
         return None
     return e.get("traffic_bytes_per_launch")
 
@@ -365,12 +373,14 @@ def copy_reference(mib, steps):
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def algorithmic_bytes(w, M, scheme="tensorwise"):
+def algorithmic_bytes(w, M, scheme="tensorwise", fused=False):
     """ABI-level bytes of one step: A read as bf16, qA written and read, scales, W read
     as FP8 with its scales, C written; plus B's quantize when it runs every call.  UE8M0
     scales are one byte each in rows padded to four bytes; rowwise scales one float per
     row of A and of W.  Delayed scaling adds, per delayed tensor, the recorded amax word
-    and the update's history, step and scale."""
+    and the update's history, step and scale.  The fused one-token step (`fused`) writes qA
+    and its scales but does not read them back.  Returns (step bytes, bytes of the GEMM
+    launch; for the fused step, its one launch's)."""
     N, K = w.n, w.k
     if w.mode == "grouped":                 # B is every expert's weight and block scales
         g = (K // 128 + 3) // 4 * 4 if scheme == "grouped-ue8m0" else 4 * (K // 128)
@@ -389,6 +399,9 @@ def algorithmic_bytes(w, M, scheme="tensorwise"):
         sa_bytes, sb_bytes = M * (K // 128) * 4, -(-N // 128) * (K // 128) * 4
     quant_a = 2 * M * K + M * K + sa_bytes
     gemm = M * K + sa_bytes + N * K + sb_bytes + 2 * M * N
+    if fused:
+        step = quant_a + N * K + sb_bytes + 2 * M * N
+        return step, step
     quant_b = (2 * N * K + N * K + sb_bytes) if w.quantize_b_per_call else 0
     if scheme == "tensorwise-delayed":
         # beyond the cast (whose scale_used write is sa_bytes): the scale read by the cast, the
@@ -571,6 +584,10 @@ def main():
     if rowwise:
         blockwise = False                   # the workload's shape with per-row scales
     scheme = scheme_of(w, args.scale_fmt, args.act_scaling, rowwise)
+    # one token with dynamic activation scales: the whole step is one fused launch
+    fused = (M == 1 and not grouped and not delayed and not w.quantize_b_per_call and not args.two_launch)
+    fused_mode = ("rowwise" if rowwise else "blockwise_ue8m0" if (blockwise and ue8m0)
+                  else "blockwise" if blockwise else "tensorwise")
     ds_a = ds_b = None
     if delayed:
         # one delayed-scaling state per quantized tensor, shared by the rotation sets: the
@@ -674,6 +691,9 @@ def main():
             fp8.fp8_gemm_scaled_tensorwise(s["qa"], s["sa"], s["qb"], s["sb"], out=s["c"])
 
     def step(s):
+        if fused:
+            fp8.fp8_gemv_dynamic(fused_mode, s["a"], s["qb"], s["sb"], out=s["c"], qa=s["qa"], sa=s["sa"])
+            return
         quantize(s)
         gemm(s)
 
@@ -734,22 +754,27 @@ def main():
     # quantizes, replayed as often as the step graph) are timed with events on the same
     # stream, and their time per step is taken off the step's.  Every GEMM thus runs right
     # after its own quantize, as in the timed steps, and no launch gap or event sits between
-    # a GEMM and the next kernel.
-    g_q = capture(R, quantize)
-    g_q.replay()
-    torch.cuda.synchronize()
-    reps = max(1, -(-K_steps // R))
-    qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in qev:
-        a.record()
+    # a GEMM and the next kernel.  The fused one-token step is one launch: its time is the
+    # step's.
+    if fused:
+        quant_ms = None
+        gemm_ms = ms_per_step
+    else:
+        g_q = capture(R, quantize)
         g_q.replay()
-        b.record()
-    torch.cuda.synchronize()
-    quant_ms = sum(a.elapsed_time(b) for a, b in qev) / (reps * R)
-    gemm_ms = ms_per_step - quant_ms
+        torch.cuda.synchronize()
+        reps = max(1, -(-K_steps // R))
+        qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in qev:
+            a.record()
+            g_q.replay()
+            b.record()
+        torch.cuda.synchronize()
+        quant_ms = sum(a.elapsed_time(b) for a, b in qev) / (reps * R)
+        gemm_ms = ms_per_step - quant_ms
 
     flops = 2.0 * M * N * K
-    step_bytes, gemm_bytes = algorithmic_bytes(w, M, scheme)
+    step_bytes, gemm_bytes = algorithmic_bytes(w, M, scheme, fused)
     decode = M <= 16
     if decode:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -767,7 +792,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, M, scheme)
+    roof["traffic"] = measured_traffic(args.workload, M, scheme, fused)
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K_steps,
@@ -778,8 +803,11 @@ def main():
                    "scale_fmt": args.scale_fmt if (blockwise or grouped) else "float32",
                    "act_scaling": args.act_scaling if not blockwise else "dynamic",
                    "in": "bf16", "out": w.out_dtype, "rotation_sets": R, "launch": "hip_graph",
-                   "gemm_ms": round(gemm_ms, 6), "quantize_ms": round(quant_ms, 6), "host_s": round(host_s, 4),
-                   "step_bytes": step_bytes},
+                   "step": ("fused: quantize + GEMV in one launch (fp8_gemv_dynamic)" if fused
+                            else "quantize launch(es), then the GEMM launch(es)"),
+                   "gemm_ms": round(gemm_ms, 6),
+                   "quantize_ms": round(quant_ms, 6) if quant_ms is not None else None,
+                   "host_s": round(host_s, 4), "step_bytes": step_bytes},
         "step_ms": step_dist,
         "roofline": roof,
     }
