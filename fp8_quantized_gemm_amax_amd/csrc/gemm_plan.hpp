@@ -44,6 +44,11 @@ constexpr int kDynWaves = 8;
 inline bool dynamic_fits(int64_t N, int64_t K) {
   return N >= 1 && K >= 1 && K <= 1024 * kDynWaves && N * K <= kLimit32;
 }
+// Its persistent form (per tensor and per row): workgroups of four waves, three per CU, each
+// wave taking every (grid waves)-th weight row; the block-scaled modes take one row per wave.
+constexpr int kDynStreamWaves = 4;
+constexpr int kDynStreamPerCu = 3;
+constexpr bool dynamic_stream(int sm) { return sm == SM_TENSOR || sm == SM_ROW; }
 
 // Whether the LDS-DMA kernels take K: whole slabs, and 256 rows of K bytes (the largest
 // tile) within 32-bit offsets.  Other K go to the register-staged kernel.

@@ -395,7 +395,8 @@ fp8_status_t fp8_debug_gemm_plan(int32_t mode, int64_t M, int64_t N, int64_t K, 
  *                           multiple of 4, padding bytes 127 (fp8_quantize_per_token_group_ue8m0);
  * and its codes qa [K] and scales sa are written bit for bit as that quantizer writes them.
  * Then c [N] = the GEMM of `mode` with M = 1: fp8_gemm_scaled_tensorwise, _rowwise,
- * _blockwise or _blockwise_ue8m0 of (qa, sa) with (qb, sb), bit for bit.
+ * _blockwise or _blockwise_ue8m0 of (qa, sa) with (qb, sb), bit for bit (where an output is
+ * NaN, both are NaN; sign and payload of an output NaN are not specified).
  *   mode : fp8_scale_mode_t.
  *   x    : bf16/fp16 [K] (device), 16-byte aligned, of `in_dt`.
  *   qb   : uint8 e4m3 [N, K] (device), 16-byte aligned; sb as the GEMM of `mode` takes it

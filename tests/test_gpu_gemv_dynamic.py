@@ -2,7 +2,7 @@
 and multiplied in one launch): its codes and scales bit for bit against the oracle's
 quantizer of the matching scheme, its output element by element against the oracle's
 product within the product tolerance, and every output bit for bit against the two-call
-path (the quantizer entry point, then the GEMM entry point), in every scale mode, for both
+path (the quantizer entry point, then the GEMM entry point; NaN outputs as NaN), in every scale mode, for both
 input and output dtypes, ragged K, the shapes that take the two-launch fallback (K > 8192),
 special inputs, graph replays and the decode workloads' full shapes."""
 
@@ -157,6 +157,14 @@ def run_two_calls(mode, xbits, dtype, qb, sb, out_dtype):
         c.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def same_outputs(a, b, out_dtype):
+    """Output bit patterns equal, except that a NaN may differ from another NaN in sign and
+    payload (which operand's NaN a multiply passes on is the compiler's operand order)."""
+    top = 0x7F80 if out_dtype == "bf16" else 0x7C00
+    na, nb = (a & 0x7FFF) > top, (b & 0x7FFF) > top
+    return bool(np.array_equal(na, nb) and np.array_equal(a[~na], b[~nb]))
+
+
 def check_all(mode, xbits, dtype, qb, sb, eb, out_dtype, label):
     qa_w, sa_w, c64, bnd = oracle_step(mode, xbits, dtype, qb, sb, eb)
     qa, sa, c, cbits = run_dynamic(mode, xbits, dtype, qb, sb, out_dtype)
@@ -167,7 +175,7 @@ def check_all(mode, xbits, dtype, qb, sb, eb, out_dtype, label):
     qa2, sa2, cbits2 = run_two_calls(mode, xbits, dtype, qb, sb, out_dtype)
     assert_bytes_equal(qa, qa2, f"{label} codes against the quantizer entry point")
     assert_bytes_equal(sa.reshape(sa2.shape), sa2, f"{label} scales against the quantizer entry point")
-    assert np.array_equal(cbits, cbits2), f"{label}: output differs from the two-call path " \
+    assert same_outputs(cbits, cbits2, out_dtype), f"{label}: output differs from the two-call path " \
         f"({int((cbits != cbits2).sum())} of {cbits.size})"
 
 
@@ -224,7 +232,7 @@ def test_dynamic_special_rows(mode):
         assert_bytes_equal(qa, qa_w, f"row {i} codes")
         assert_bytes_equal(sa.reshape(sa_w.shape), sa_w, f"row {i} scales")
         qa2, sa2, cbits2 = run_two_calls(mode, xbits, "bf16", qb, sb, "bf16")
-        assert np.array_equal(cbits, cbits2), f"row {i}: output differs from the two-call path"
+        assert same_outputs(cbits, cbits2, "bf16"), f"row {i}: output differs from the two-call path"
         if i < 2:
             r = oracle.check_gemm(c, c64, bnd, "bf16")
             assert r["ok"], (i, r)
@@ -296,7 +304,7 @@ def test_dynamic_workload_shapes(workload, mode):
     N = qb.shape[0]
     qa, sa, c, cbits = run_dynamic(mode, xbits, "bf16", qb, sb, "bf16")
     qa2, sa2, cbits2 = run_two_calls(mode, xbits, "bf16", qb, sb, "bf16")
-    assert np.array_equal(cbits, cbits2), f"{int((cbits != cbits2).sum())} outputs differ from the two-call path"
+    assert same_outputs(cbits, cbits2, "bf16"), f"{int((cbits != cbits2).sum())} outputs differ from the two-call path"
     qa_w, sa_w, s = oracle_quant(mode, xbits, "bf16")
     assert_bytes_equal(qa, qa_w, "codes")
     assert_bytes_equal(sa.reshape(sa_w.shape), sa_w, "scales")
