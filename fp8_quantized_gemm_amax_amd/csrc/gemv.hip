@@ -451,7 +451,9 @@ __global__ __launch_bounds__(256) void gemv1_stream_kernel(
   auto fetch = [&](int row, int ch) {                         // chunk ch of row (row >= N: zeros)
     const int col = ch * 1024 + lane * 16;
     const bool in = (row < N) & (col < K);                    // K % 16 == 0
-    wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? static_cast<uint32_t>(row * K + col) : kOOB, 0, 0);
+    // unsigned: rows past N (their offsets are not used) would overflow int
+    wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(
+        wr, in ? static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(col) : kOOB, 0, 0);
     if constexpr (BLOCKWISE) {
       const int g = min(col, K - 1) >> 7;
       sbv[ch] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -558,7 +560,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv1_dynamic_kernel(
   auto fetch = [&](int row, int ch) {                         // chunk ch of a row (row >= N: zeros)
     const int col = ch * 1024 + lane * 16;
     const bool in = (row < N) & (col < K);
-    wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? static_cast<uint32_t>(row * K + col) : kOOB, 0, 0);
+    // unsigned: rows past N (their offsets are not used) would overflow int
+    wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(
+        wr, in ? static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(col) : kOOB, 0, 0);
     if constexpr (GROUPS) {
       const int g = col >> 7;
       sbv[ch] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
