@@ -181,8 +181,11 @@ def check_all(mode, xbits, dtype, qb, sb, eb, out_dtype, label):
 
 # K: one chunk and less, ragged chunks (1152, 2944), whole chunks (4096, 8192), the largest
 # one-launch K and the two-launch fallback beyond it (8320, 12288); N: one row, ragged
-# workgroups (7, 130, 257: eight weight rows per workgroup), a weight block straddled
-SHAPES = [(1, 128), (7, 1152), (130, 4096), (257, 7168), (33, 8192), (64, 2944), (5, 8320), (3, 12288)]
+# workgroups (7, 130, 257: eight weight rows per workgroup), a weight block straddled, and
+# more rows than the persistent form has waves (3072), so that waves take one, two or five
+# rows and the last refill runs past N (3100, 12289)
+SHAPES = [(1, 128), (7, 1152), (130, 4096), (257, 7168), (33, 8192), (64, 2944), (5, 8320), (3, 12288),
+          (3100, 1024), (12289, 256)]
 SHAPES_K16 = [(40, 16), (9, 1040), (17, 8208)]          # K % 128 != 0: per tensor and per row only
 
 
