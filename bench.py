@@ -2,9 +2,10 @@
 
 One step = the whole hot path over one batch of synthetic input: amax + scale + cast of
 the activations (per tensor, or per 1x128 token group), then the FP8 x FP8 GEMM with
-float32 accumulation and the scale epilogue.  Weights are quantized once before timing
-(as a serving stack does at load time), except in the small per-tensor workload, where
-both operands are quantized on every call.
+float32 accumulation and the scale epilogue; for one token with dynamic scales both in one
+launch (fp8_gemv_dynamic; --two-launch times the pair).  Weights are quantized once before
+timing (as a serving stack does at load time), except in the small per-tensor workload,
+where both operands are quantized on every call.
 
 Inputs stay resident in HBM; each step reads a different copy of the input set from a
 rotation whose footprint exceeds 1 GiB, so reads come from HBM rather than the 256 MB
@@ -697,17 +698,17 @@ def main():
         quantize(s)
         gemm(s)
 
-    # eager warm-up (first launches, lazy initialisation; with delayed scaling at least two
-    # intervals, so the scale has reached its steady state), then one eager reference output
-    for i in range(max(1, args.warmup, 2 * DELAYED_INTERVAL if delayed else 1)):
+    # eager warm-up: the first launches and lazy initialisation, at most one step per rotation
+    # set (with delayed scaling at least two intervals, so the scale has reached its steady
+    # state); then one eager reference output
+    for i in range(max(1, min(args.warmup, R), 2 * DELAYED_INTERVAL if delayed else 1)):
         step(sets[i % R])
     step(sets[0])
     torch.cuda.synchronize()
     ref_c = sets[0]["c"].clone()
 
     # HIP graphs: one replay runs `R` steps (one per rotation set); a tail graph runs the
-    # remaining K mod R, so exactly K steps are timed.  Every graph is replayed once before
-    # the timed region.
+    # remaining K mod R, so exactly K steps are timed.
     K_steps = args.steps
     def capture(n, fn, first=0):
         g = torch.cuda.CUDAGraph()
@@ -718,10 +719,15 @@ def main():
     n_full, tail = divmod(K_steps, R)
     g_full = capture(R, step) if n_full else None
     g_tail = capture(tail, step) if tail else None
-    for _ in range(2):                      # graph warm-up replays
-        for g in (g_full, g_tail):
-            if g is not None:
-                g.replay()
+    # graph warm-up: the W untimed steps as replays, back to back, so that the GPU runs them
+    # under load as it runs the timed steps (eager launches leave it idle between steps);
+    # every graph is replayed at least twice
+    warm, per_warm = (g_full, R) if g_full is not None else (g_tail, tail)
+    for _ in range(max(2, -(-args.warmup // per_warm))):
+        warm.replay()
+    if g_full is not None and g_tail is not None:
+        g_tail.replay()
+        g_tail.replay()
     torch.cuda.synchronize()
 
     # timed region: an event pair around every replay; the per-step time of a replay is its
