@@ -243,15 +243,14 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
 // Large-tile kernel: slabs move global -> LDS by buffer_load ... lds (LDS DMA), so no VGPRs
 // stage them and no masked branches guard them: the buffer range check returns zeros for
 // rows past M or N; K must be a multiple of 128.
-// Two stages live in distinct __shared__ arrays and the loop is unrolled by two, so the
-// compiler can tell the stage being read from the one being filled and keeps the next
-// slab's DMA in flight across the current slab's MFMAs (one barrier per slab).
+// The DMA is inline asm, so the compiler does not wait for it before the fragment reads;
+// the kernel orders them itself (wait_vmcnt for its own DMA of the slab, then a barrier),
+// and the next slabs' DMA stays in flight across the current slab's MFMAs.
 //
 // DMA layout: each wave instruction g writes 64 consecutive 16-byte chunks, rows 8g .. 8g+7;
-// lane i of the instruction fetches logical chunk (i % 8) ^ swz(8g + i / 8) of its row,
-// which puts chunk c of row r at position c ^ swz(r) - the swizzle the fragment reads use.
-// swz(8g + r') = 4 (g & 1) + r' / 2, so a lane has one source offset for even and one for
-// odd instructions.
+// lane i of the instruction fetches logical chunk dma_chunk(i, g & 1) = (i % 8) ^
+// swz(8g + i / 8) of its row, which puts chunk c of row r at position c ^ swz(r) - the
+// swizzle the fragment reads use (gemm_common.hpp).
 //
 // Tile order: workgroup b runs on XCD b % 8; consecutive tiles of a grouped order
 // (groups of kGroupM tile rows) are given to the same XCD so its L2 serves their shared
@@ -316,7 +315,7 @@ __global__ __launch_bounds__((dma_threads<BM, BN, WM, WN>())) void gemm_dma_kern
   const v4i ra = make_rsrc(qa + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(BM, M - m0) * K));
   const v4i rb = make_rsrc(qb + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(min(BN, N - n0) * K));
   // logical chunk this lane fetches in even and in odd DMA instructions
-  const int lc0 = (lane & 7) ^ (lane >> 4), lc1 = lc0 ^ 4;
+  const int lc0 = dma_chunk(lane, 0), lc1 = dma_chunk(lane, 1);
   const uint32_t row_off = static_cast<uint32_t>(((w * IA) * 8 + (lane >> 3)) * K);
   const uint32_t row_off_b = static_cast<uint32_t>(((w * IB) * 8 + (lane >> 3)) * K);
   const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
@@ -603,7 +602,7 @@ __device__ __forceinline__ void skinny_body(
     if constexpr (E8M0) rs = make_rsrc(sa_, static_cast<uint32_t>(M * KG4));
     else if constexpr (BLOCKWISE) rs = make_rsrc(sa, static_cast<uint32_t>(M * KG * 4));
     // instruction j fetches rows 8j .. 8j + 7; lane i takes logical chunk (i % 8) ^ swz(row)
-    const int lc0 = (lane & 7) ^ (lane >> 4), lc1 = lc0 ^ 4;
+    const int lc0 = dma_chunk(lane, 0), lc1 = dma_chunk(lane, 1);
     const uint32_t c_even = static_cast<uint32_t>(lc0 * 16), c_odd = static_cast<uint32_t>(lc1 * 16);
     const uint32_t row_off = static_cast<uint32_t>((lane >> 3) * K);
     auto issue = [&](int s, int st, bool scales) {

@@ -18,10 +18,22 @@ constexpr int kSlab = 128;
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past any range: the load returns zeros
 
 // LDS layout of a slab tile, [rows][128 B]: the 16-byte chunk c of row r is stored at chunk
-// position c ^ swz(r).  A row is half of the 64 banks, so rows r and r + 1 start on opposite
-// halves and the swizzle spreads each pair over the eight 16-byte bank groups: the 16 lanes
-// reading one chunk column of 16 consecutive rows hit 16 distinct bank groups.
-__host__ __device__ constexpr int swz(int row) { return (row >> 1) & 7; }
+// position c ^ swz(r), swz being linear (over GF(2)) in the row's low four bits.  A fragment
+// read takes one 16-byte chunk from each of 16 consecutive rows per group of 16 lanes; with
+// this swizzle no group of a ds_read_b128 hits an LDS bank twice.  Measured on gfx950 with
+// the bank-conflict counter (SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE): 4 LDS cycles per
+// fragment read, against 8 with the swizzle (r >> 1) & 7, r & 7 or a row rotation, and 16
+// with none.  Each row keeps its own 128 bytes, so an LDS DMA instruction still writes eight
+// whole rows.
+__host__ __device__ constexpr int swz(int row) {
+  return ((row & 1) ? 1 : 0) ^ ((row & 2) ? 4 : 0) ^ ((row & 4) ? 1 : 0) ^ ((row & 8) ? 3 : 0);
+}
+
+// The logical chunk lane `lane` of an LDS DMA instruction fetches: instruction g writes rows
+// 8g .. 8g + 7 as one contiguous KB, lane i at row 8g + i / 8, chunk position i % 8.  swz
+// depends on bit 3 of the row only through g's parity, so a lane has one chunk for even and
+// one for odd instructions.
+__host__ __device__ constexpr int dma_chunk(int lane, int odd) { return (lane & 7) ^ swz(8 * odd + (lane >> 3)); }
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz = blgp = 0: both operands e4m3; E8M0 scale 127 = 2^0 on both.
