@@ -300,7 +300,8 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(
     const bool in = (i < nch) & (col < K);                   // K % 16 == 0
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
-      wv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, (in & (r < rows)) ? static_cast<uint32_t>(r * K + col) : kOOB, 0, 0);
+      wv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, (in & (r < rows)) ? static_cast<uint32_t>(r * K + col) : kOOB, 0,
+                                                       kStreamOnce);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
       av[u][m] = __builtin_amdgcn_raw_buffer_load_b128(ar, (in & (m < M)) ? static_cast<uint32_t>(m * K + col) : kOOB, 0, 0);
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(256) void gemv1_stream_kernel(
     const bool in = (row < N) & (col < K);                    // K % 16 == 0
     // unsigned: rows past N (their offsets are not used) would overflow int
     wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(
-        wr, in ? static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(col) : kOOB, 0, 0);
+        wr, in ? static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(col) : kOOB, 0, kStreamOnce);
     if constexpr (BLOCKWISE) {
       const int g = min(col, K - 1) >> 7;
       sbv[ch] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv1_dynamic_kernel(
     const bool in = (row < N) & (col < K);
     // unsigned: rows past N (their offsets are not used) would overflow int
     wv[ch] = __builtin_amdgcn_raw_buffer_load_b128(
-        wr, in ? static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(col) : kOOB, 0, 0);
+        wr, in ? static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(col) : kOOB, 0, kStreamOnce);
     if constexpr (GROUPS) {
       const int g = col >> 7;
       sbv[ch] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
