@@ -942,7 +942,8 @@ bool run_launch(const fp8_gemm_launch_t& L, const uint8_t* qa, const void* sa, c
         if (L.paired != (PAIR ? 1 : 0)) return false;
         launch_tile<256, 256, 64, 128, SM, OUT, 2, PAIR>(L, qa, sa, qb, sb, M, N, K, c, s);
       } else if (L.tile_m == 256) {
-        launch_tile<256, 128, 64, 64, SM, OUT, 2, false>(L, qa, sa, qb, sb, M, N, K, c, s);
+        if (L.variant == 3) launch_tile<256, 128, 64, 64, SM, OUT, 3, false>(L, qa, sa, qb, sb, M, N, K, c, s);
+        else launch_tile<256, 128, 64, 64, SM, OUT, 2, false>(L, qa, sa, qb, sb, M, N, K, c, s);
       } else if (L.tile_n == 96) {
         if constexpr (slab_scaled(SM)) return false;   // 48-column waves: no per-block scales
         else launch_tile<128, 96, 64, 48, SM, OUT, 3, false>(L, qa, sa, qb, sb, M, N, K, c, s);

@@ -131,7 +131,7 @@ def test_every_accepted_shape_has_a_plan_within_32_bit_addressing(mode):
     expect = {"gemv_valu", "gemv_mfma", "staged", "skinny", "tile"} | ({"gemv_stream"} if mode == "blockwise" else set())
     assert kinds == expect
     tiles = {(s[1], s[2], s[3]) for s in seen if s[0] == "tile"}
-    assert tiles == {(256, 256, 2), (256, 128, 2), (128, 128, 2), (128, 128, 3)} | (
+    assert tiles == {(256, 256, 2), (256, 128, 2), (256, 128, 3), (128, 128, 2), (128, 128, 3)} | (
         set() if SLAB[mode] else {(128, 96, 3)})
     assert {(s[1], s[2]) for s in seen if s[0] == "staged"} == {(16, 256), (128, 128)}
     assert {s[3] for s in seen if s[0] == "skinny"} == {2, 4, 8}
@@ -142,15 +142,20 @@ def test_large_tile_rounds_and_tail():
     """DeepSeek-V3 up-projection, 4096 tokens: 16 x 72 tiles of 256x256 are 4.5 rounds on 256
     CUs; 64 tile columns make 4 whole rounds and the last 8 columns (2048 outputs) run as
     256 tiles of 256x128, one round."""
+    # (a whole round of tail tiles over 56 slabs: three stages)
     plan = fp8.fp8_debug_gemm_plan("blockwise", 4096, 18432, 7168)
-    assert [(L["kernel"], L["tile_m"], L["tile_n"], L["grid"], L["n_begin"], L["n_end"], L["paired"])
-            for L in plan] == [("tile", 256, 256, 1024, 0, 16384, 0), ("tile", 256, 128, 256, 16384, 18432, 0)]
+    assert [(L["kernel"], L["tile_m"], L["tile_n"], L["variant"], L["grid"], L["n_begin"], L["n_end"], L["paired"])
+            for L in plan] == [("tile", 256, 256, 2, 1024, 0, 16384, 0), ("tile", 256, 128, 3, 256, 16384, 18432, 0)]
     plan = fp8.fp8_debug_gemm_plan("blockwise_ue8m0", 4096, 18432, 7168)
     assert plan[0]["paired"] == 1 and plan[1]["paired"] == 0
     # Llama-3-8B MLP: 16 x 56 = 896 tiles, 3.5 rounds; 48 columns make 3 rounds, the last 8
-    # columns 128 tiles of 256x128 (half a round)
+    # columns 256 tiles of 256x128, one round, over 32 slabs: two stages
     plan = fp8.fp8_debug_gemm_plan("blockwise", 4096, 14336, 4096)
-    assert [(L["grid"], L["n_begin"], L["n_end"]) for L in plan] == [(768, 0, 12288), (256, 12288, 14336)]
+    assert [(L["grid"], L["variant"], L["n_begin"], L["n_end"]) for L in plan] == [(768, 2, 0, 12288), (256, 2, 12288, 14336)]
+    # DeepSeek-V3, 2048 tokens: 8 x 72 tiles, 2.25 rounds; the last 8 columns are 128 tiles
+    # of 256x128 (half a round): two stages
+    plan = fp8.fp8_debug_gemm_plan("blockwise", 2048, 18432, 7168)
+    assert [(L["grid"], L["variant"], L["n_begin"], L["n_end"]) for L in plan] == [(512, 2, 0, 16384), (128, 2, 16384, 18432)]
     # a whole number of rounds: one launch
     plan = fp8.fp8_debug_gemm_plan("tensorwise", 4096, 4096, 4096)
     assert [(L["tile_m"], L["tile_n"], L["grid"]) for L in plan] == [(256, 256, 256)]

@@ -337,14 +337,17 @@ def test_workload_prefill_sampled(name):
 
 @pytest.mark.parametrize("scale_fmt", ["float32", "ue8m0"])
 def test_large_tile_full_output_at_production_k(scale_fmt):
-    """Every output of a 4096 x 4352 x 7168 blockwise product: 56 slabs through the
+    """Every output of a 4096 x 6100 x 7168 blockwise product: 56 slabs through the
     two-stage LDS ring of the 256x256 kernel, K = 7168 as in the DeepSeek-V3 workload.  Its
-    17 x 16 tiles are one round of 256 tiles plus one tile column, which the dispatcher
-    runs as a second launch of 256x128 tiles, so both launches are checked whole.  The
-    operands are those of the workload's own generators (Student-t activations per 1x128
-    group, 128x128 weight blocks)."""
+    16 x 24 tiles are one round of 256 tiles plus 8 tile columns, which the dispatcher runs
+    as a second launch of 256x128 tiles, a whole round of them and so with three stages
+    (the last column ragged), so both launches are checked whole.  The operands are those
+    of the workload's own generators (Student-t activations per 1x128 group, 128x128
+    weight blocks)."""
     rng = np.random.default_rng(77)
-    M, N, K = 4096, 4352, 7168
+    M, N, K = 4096, 6100, 7168
+    plan = fp8.fp8_debug_gemm_plan("blockwise" if scale_fmt == "float32" else "blockwise_ue8m0", M, N, K)
+    assert [(L["tile_m"], L["tile_n"], L["variant"], L["grid"]) for L in plan] == [(256, 256, 2, 256), (256, 128, 3, 256)]
     a_bits = wl.to_bf16_bits(rng.standard_t(4, (M, K)))
     b_bits = wl.to_bf16_bits(0.02 * rng.standard_normal((N, K)))
     if scale_fmt == "float32":
