@@ -158,7 +158,7 @@ inline fp8_gemm_plan_t plan_gemm(int sm, int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
   if (big_tiles >= kCus) {
     // whole rounds of 256x256 tiles (one per CU), and when the tile columns left over make
-    // at most half a round, those columns as 256x128 tiles in a second launch, so that the
+    // at most half a round, those columns as smaller tiles in a second launch, so that the
     // last round is not half empty.  Columns split on whole tiles, so the second launch's
     // weight rows, block scales and C columns are plain offsets.  Paired DMA issue (one
     // wave of each SIMD pair issues the slab's DMA for both) measured faster where no
@@ -172,13 +172,21 @@ inline fp8_gemm_plan_t plan_gemm(int sm, int64_t M, int64_t N, int64_t K) {
     const int64_t n_main = std::min(N, cols_main * 256);
     l = tile_launch(sm, M, 0, n_main, K, 256, 256, 64, 128, 2, sm != SM_BLOCK);
     if (n_main < N) {
-      // The 256x128 tiles take a third stage where they fill a whole round and K spans 48
-      // slabs or more: measured 8-19% faster there (DeepSeek-V3 up-projection, 4096
-      // tokens, every scale mode), 2-4% slower over 32 slabs or with half a round.
+      // At most half a round of 256x128 tiles leaves half the CUs idle: such a tail runs as
+      // 128x128 tiles (eight 64x32 waves, three stages), at most one round of them; measured
+      // 8-16% faster over the whole GEMM (DeepSeek-V3 up-projection at 1024 and 2048
+      // tokens, 4096 x 4352 x 7168; every scale mode).  A larger tail keeps 256x128 tiles,
+      // with a third stage where they fill a whole round and K spans 48 slabs or more:
+      // measured 8-19% faster there alone (DeepSeek-V3 up-projection, 4096 tokens, every
+      // scale mode), 2-4% slower over 32 slabs or with half a round.
       const int64_t tail_tiles = tiles_m * cdiv(N - n_main, 128);
-      const int ns = (tail_tiles >= kCus && K / kSlabK >= 48) ? 3 : 2;
       p.launches = 2;
-      p.launch[1] = tile_launch(sm, M, n_main, N, K, 256, 128, 64, 64, ns, false);
+      if (2 * tail_tiles <= kCus) {
+        p.launch[1] = tile_launch(sm, M, n_main, N, K, 128, 128, 64, 32, 3, false);
+      } else {
+        const int ns = (tail_tiles >= kCus && K / kSlabK >= 48) ? 3 : 2;
+        p.launch[1] = tile_launch(sm, M, n_main, N, K, 256, 128, 64, 64, ns, false);
+      }
     }
   } else if (tiles > kCus) {
     l = tile_launch(sm, M, 0, N, K, 128, 128, 64, 64, 2, false);

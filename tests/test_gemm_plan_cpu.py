@@ -104,6 +104,7 @@ def check_plan(mode, M, N, K, plan):
             assert L["max_range"] >= min(bm, M) * K and L["max_range"] >= min(bn, n) * K
             if L["n_begin"] > 0:
                 assert L["n_begin"] % 128 == 0              # weight blocks and scales are plain offsets
+                assert L["grid"] <= 256                     # a tail launch is at most one round
             if SLAB[mode]:
                 assert 128 % (bn // (L["waves"] // (bm // 64))) == 0   # a wave's columns in one weight block
             if bn == 96:                                    # one round of them, where 128x128 is one round too
@@ -152,10 +153,15 @@ def test_large_tile_rounds_and_tail():
     # columns 256 tiles of 256x128, one round, over 32 slabs: two stages
     plan = fp8.fp8_debug_gemm_plan("blockwise", 4096, 14336, 4096)
     assert [(L["grid"], L["variant"], L["n_begin"], L["n_end"]) for L in plan] == [(768, 2, 0, 12288), (256, 2, 12288, 14336)]
-    # DeepSeek-V3, 2048 tokens: 8 x 72 tiles, 2.25 rounds; the last 8 columns are 128 tiles
-    # of 256x128 (half a round): two stages
+    # DeepSeek-V3, 2048 tokens: 8 x 72 tiles, 2.25 rounds; the last 8 columns would be 128
+    # tiles of 256x128 (half a round), so they run as one round of 256 tiles of 128x128
+    # (eight waves, three stages)
     plan = fp8.fp8_debug_gemm_plan("blockwise", 2048, 18432, 7168)
-    assert [(L["grid"], L["variant"], L["n_begin"], L["n_end"]) for L in plan] == [(512, 2, 0, 16384), (128, 2, 16384, 18432)]
+    assert [(L["tile_m"], L["tile_n"], L["waves"], L["grid"], L["variant"], L["n_begin"], L["n_end"]) for L in plan] == [
+        (256, 256, 8, 512, 2, 0, 16384), (128, 128, 8, 256, 3, 16384, 18432)]
+    # a small tail: one 256-column of 4096 x 4352 as 32 x 2 tiles of 128x128
+    plan = fp8.fp8_debug_gemm_plan("tensorwise", 4096, 4352, 7168)
+    assert [(L["tile_m"], L["tile_n"], L["grid"], L["n_begin"]) for L in plan] == [(256, 256, 256, 0), (128, 128, 64, 4096)]
     # a whole number of rounds: one launch
     plan = fp8.fp8_debug_gemm_plan("tensorwise", 4096, 4096, 4096)
     assert [(L["tile_m"], L["tile_n"], L["grid"]) for L in plan] == [(256, 256, 256)]

@@ -110,8 +110,10 @@ TILE_CHOICES = [
     ("tensorwise", 250, 14000, 256, [("tile", 128, 128)]),
     ("blockwise", 300, 1000, 384, [("tile", 128, 128)]),
     ("tensorwise", 1030, 4100, 384, [("tile", 128, 128)]),
-    ("blockwise", 2049, 8195, 384, [("tile", 256, 256), ("tile", 256, 128)]),
-    ("tensorwise", 2050, 8200, 256, [("tile", 256, 256), ("tile", 256, 128)]),
+    ("blockwise", 2049, 8195, 384, [("tile", 256, 256), ("tile", 128, 128)]),
+    ("tensorwise", 2050, 8200, 256, [("tile", 256, 256), ("tile", 128, 128)]),
+    ("blockwise", 4095, 6100, 384, [("tile", 256, 256), ("tile", 256, 128)]),
+    ("tensorwise", 4095, 6100, 256, [("tile", 256, 256), ("tile", 256, 128)]),
 ]
 
 
