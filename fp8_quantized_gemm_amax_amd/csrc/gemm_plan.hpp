@@ -174,11 +174,12 @@ inline fp8_gemm_plan_t plan_gemm(int sm, int64_t M, int64_t N, int64_t K) {
     if (n_main < N) {
       // At most half a round of 256x128 tiles leaves half the CUs idle: such a tail runs as
       // 128x128 tiles (eight 64x32 waves, three stages), at most one round of them; measured
-      // 8-16% faster over the whole GEMM (DeepSeek-V3 up-projection at 1024 and 2048
-      // tokens, 4096 x 4352 x 7168; every scale mode).  A larger tail keeps 256x128 tiles,
-      // with a third stage where they fill a whole round and K spans 48 slabs or more:
-      // measured 8-19% faster there alone (DeepSeek-V3 up-projection, 4096 tokens, every
-      // scale mode), 2-4% slower over 32 slabs or with half a round.
+      // 6-16% faster over the whole GEMM (DeepSeek-V3 up-projection at 1024 and 2048
+      // tokens, 4096 x 4352 x 7168; float32 block, UE8M0 and per-tensor scales).  A larger
+      // tail keeps 256x128 tiles, with a third stage where they fill a whole round and K
+      // spans 48 slabs or more: measured 8-19% faster there alone (DeepSeek-V3
+      // up-projection, 4096 tokens, every scale mode), 2-4% slower over 32 slabs or with
+      // half a round.
       const int64_t tail_tiles = tiles_m * cdiv(N - n_main, 128);
       p.launches = 2;
       if (2 * tail_tiles <= kCus) {
