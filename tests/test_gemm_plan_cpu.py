@@ -105,6 +105,12 @@ def check_plan(mode, M, N, K, plan):
             if L["n_begin"] > 0:
                 assert L["n_begin"] % 128 == 0              # weight blocks and scales are plain offsets
                 assert L["grid"] <= 256                     # a tail launch is at most one round
+                wide = cdiv(M, 256) * cdiv(n, 128)          # the tail in 256x128 tiles
+                if (bm, bn) == (128, 128):                  # those would fill at most half a round
+                    assert 2 * wide <= 256 and (L["waves"], L["variant"]) == (8, 3)
+                else:
+                    assert (bm, bn) == (256, 128) and 2 * wide > 256
+                    assert L["variant"] == (3 if wide >= 256 and K // 128 >= 48 else 2)
             if SLAB[mode]:
                 assert 128 % (bn // (L["waves"] // (bm // 64))) == 0   # a wave's columns in one weight block
             if bn == 96:                                    # one round of them, where 128x128 is one round too
@@ -115,7 +121,7 @@ def check_plan(mode, M, N, K, plan):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_every_accepted_shape_has_a_plan_within_32_bit_addressing(mode):
-    seen = set()
+    seen, tails = set(), set()
     for M, N, K in shapes(mode):
         if too_large(M, N, K):
             with pytest.raises(fp8.Fp8Error) as e:
@@ -127,6 +133,8 @@ def test_every_accepted_shape_has_a_plan_within_32_bit_addressing(mode):
         for L in plan:
             seen.add((L["kernel"], L["tile_m"] if L["kernel"] in ("tile", "staged") else 0,
                       L["tile_n"] if L["kernel"] in ("tile", "staged") else 0, L["variant"]))
+            if L["n_begin"] > 0:
+                tails.add((L["tile_m"], L["tile_n"], L["variant"]))
     # every kernel and tile the dispatcher has was reached by the sweep
     kinds = {s[0] for s in seen}
     expect = {"gemv_valu", "gemv_mfma", "staged", "skinny", "tile"} | ({"gemv_stream"} if mode == "blockwise" else set())
@@ -134,6 +142,7 @@ def test_every_accepted_shape_has_a_plan_within_32_bit_addressing(mode):
     tiles = {(s[1], s[2], s[3]) for s in seen if s[0] == "tile"}
     assert tiles == {(256, 256, 2), (256, 128, 2), (256, 128, 3), (128, 128, 2), (128, 128, 3)} | (
         set() if SLAB[mode] else {(128, 96, 3)})
+    assert tails == {(128, 128, 3), (256, 128, 2), (256, 128, 3)}   # every kind of tail launch
     assert {(s[1], s[2]) for s in seen if s[0] == "staged"} == {(16, 256), (128, 128)}
     assert {s[3] for s in seen if s[0] == "skinny"} == {2, 4, 8}
     assert {s[3] for s in seen if s[0] == "gemv_mfma"} == {1, 2}
