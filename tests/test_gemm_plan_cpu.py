@@ -106,7 +106,11 @@ def check_plan(mode, M, N, K, plan):
                 assert L["n_begin"] % 128 == 0              # weight blocks and scales are plain offsets
                 assert L["grid"] <= 256                     # a tail launch is at most one round
                 wide = cdiv(M, 256) * cdiv(n, 128)          # the tail in 256x128 tiles
-                if (bm, bn) == (128, 128):                  # those would fill at most half a round
+                if plan[0]["tile_m"] == 128:                # after whole rounds of 128x128 tiles
+                    assert mode != "blockwise" and (bm, bn, L["waves"], L["variant"]) == (128, 128, 8, 3)
+                    r = plan[0]["grid"] % 512                # whole rounds, short by less than a column
+                    assert 64 <= L["grid"] and (r == 0 or r > 512 - cdiv(M, 128))
+                elif (bm, bn) == (128, 128):                # 256x128 tiles would fill at most half a round
                     assert 2 * wide <= 256 and (L["waves"], L["variant"]) == (8, 3)
                 else:
                     assert (bm, bn) == (256, 128) and 2 * wide > 256

@@ -110,6 +110,8 @@ TILE_CHOICES = [
     ("tensorwise", 250, 14000, 256, [("tile", 128, 128)]),
     ("blockwise", 300, 1000, 384, [("tile", 128, 128)]),
     ("tensorwise", 1030, 4100, 384, [("tile", 128, 128)]),
+    ("tensorwise", 520, 18000, 256, [("tile", 128, 128), ("tile", 128, 128)]),
+    ("blockwise", 520, 18000, 256, [("tile", 128, 128)]),
     ("blockwise", 2049, 8195, 384, [("tile", 256, 256), ("tile", 128, 128)]),
     ("tensorwise", 2050, 8200, 256, [("tile", 256, 256), ("tile", 128, 128)]),
     ("blockwise", 4095, 6100, 384, [("tile", 256, 256), ("tile", 256, 128)]),
