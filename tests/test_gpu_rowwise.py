@@ -132,7 +132,7 @@ def check(got, qa, sa, qb, sb, out_dtype, label):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (1, 300, 4096), (1, 37, 2192), (3, 17, 48), (5, 290, 656),
                                    (16, 64, 128), (17, 130, 272), (33, 1000, 2048), (65, 4100, 256),
                                    (128, 12300, 384), (130, 257, 528), (300, 520, 256), (600, 600, 384),
-                                   (1030, 4100, 384), (2050, 8200, 256)])
+                                   (1030, 4100, 384), (2050, 8200, 256), (520, 18000, 256)])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 def test_rowwise_gemm_shapes(M, N, K, out_dtype):
     qa, sa, qb, sb = random_rowwise_case(M, N, K, M * 31 + N * 7 + K)

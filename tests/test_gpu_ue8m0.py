@@ -135,9 +135,10 @@ def test_few_token_scale_block_staging(M, N, K):
     check(run_gemm(qa, ea, qb, eb, "bf16"), qa, ea, qb, eb, "bf16", f"staging {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(2050, 8200, 256), (1030, 4100, 384), (520, 33000, 128)])
+@pytest.mark.parametrize("M,N,K", [(2050, 8200, 256), (1030, 4100, 384), (520, 33000, 128), (520, 18000, 256)])
 def test_large_tile_paths(M, N, K):
-    """The 256x256 tile (at least one tile per CU) and the four-wave 128x128 tile."""
+    """The 256x256 tile (at least one tile per CU) with its 128x128 tail, the four-wave
+    128x128 tile, and whole rounds of it with a tail launch of eight-wave 128x128 tiles."""
     qa, ea, qb, eb = random_case(M, N, K, M + N + K)
     check(run_gemm(qa, ea, qb, eb, "bf16"), qa, ea, qb, eb, "bf16", f"{M}x{N}x{K}")
 
